@@ -1,0 +1,211 @@
+"""fp64 CPU oracle for the exact scaled-dot-product attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the CPU-baseline
+leg of the bench may call this module; the product path (the ``libfa`` C
+library and its Python binding) never imports, links or runs it, and this
+module imports nothing from the product path.
+
+What it computes is the plain definition, written out and materialised on
+purpose (it is the "standard" schedule that the tiled method avoids):
+
+* "Softmax does not need the matrix" (sir-teo.github.io), opening equation
+  and section *Carry the Normalizer*: scores s_j = q.k_j / sqrt(d), the stable
+  softmax p_j = exp(s_j - m) / sum_i exp(s_i - m) with m = max_i s_i, and the
+  output o = sum_j p_j v_j.
+* "Understanding FlashAttention Pt 1: Personal Notes", section 0.2 Notation:
+  S = Q K^T / sqrt(d) (+ B), P = softmax_row(S), O = P V; and the three-step
+  standard algorithm of its introduction (form S, form P, form O).
+
+Readings taken where the pages are silent:
+
+* the caller passes ``scale`` (the pages' 1/sqrt(d) is the usual value);
+* causal masking is top-left: query i sees key j iff j <= i (indices local to
+  the sequence), and key j must exist (j < Lk);
+* grouped-query attention groups contiguous heads: q-head h reads kv-head
+  h // (Hq // Hkv);
+* the retained row statistic is the natural-log log-sum-exp of the scaled,
+  visible scores: LSE_i = m_i + log(sum_j exp(S_ij - m_i));
+* a row that sees no key has O = 0 and LSE = -inf;
+* no additive bias B, and V has the same width d as Q and K.
+
+Everything is float64. bf16 and fp32 inputs are exactly representable in
+float64, so the upcast adds no error.
+
+Memory layouts (token-major, row-major, contiguous), the same ones the C ABI
+uses:
+
+* fixed length: q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d],
+  O [B, Nq, Hq, d], LSE [B, Hq, Nq];
+* packed variable length (``cu_seqlens`` = offsets [nseq + 1]):
+  q [T, Hq, d], k and v [T, Hkv, d], O [T, Hq, d], LSE [Hq, T], with
+  sequence s occupying tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of both the
+  query and the key side (self-attention), never attending across sequences.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Rows of S materialised at once. It bounds host memory only; every row is
+# still formed whole, exactly as the definition reads.
+ROW_CHUNK = 1024
+
+
+def kv_head_of(h: int, hq: int, hkv: int) -> int:
+    """K/V head read by query head ``h`` (grouped-query attention).
+
+    "Softmax does not need the matrix", section *Quadratic Time Did Not
+    Vanish*, names grouped-query attention; "Understanding FlashAttention
+    Pt 1", section 1.1, lists MQA/GQA as compatible. Reading: the Hq/Hkv query
+    heads of one group are contiguous, so h -> h // (Hq // Hkv).
+    """
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"Hq={hq} must be a positive multiple of Hkv={hkv}")
+    return h // (hq // hkv)
+
+
+def visible_mask(rows: np.ndarray, lk: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), lk]: True where query ``rows[r]`` may see key j.
+
+    Causal reading: top-left lower-triangular, j <= i, indices local to the
+    sequence ("Understanding FlashAttention Pt 1", section 3.5 title, causal
+    masking; the body of that section is not in the pages, so the plain
+    lower-triangular mask is taken).
+    """
+    j = np.arange(lk)[None, :]
+    i = np.asarray(rows)[:, None]
+    if causal:
+        return j <= i
+    return np.broadcast_to(j >= 0, (len(rows), lk))
+
+
+def scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * q_rows K^T, materialised ("Understanding FlashAttention
+    Pt 1", section 0.2: S = Q K^T / sqrt(d); "Softmax does not need the
+    matrix", s_j = q^T k_j / sqrt(d))."""
+    return (q_rows @ k.T) * scale
+
+
+def softmax_rows(s: np.ndarray):
+    """Stable row softmax of a materialised score block.
+
+    "Softmax does not need the matrix", section *Carry the Normalizer*:
+    p_j = exp(s_j - m) / sum_i exp(s_i - m), m = max_i s_i. Masked entries
+    arrive as -inf and get probability 0. Returns (P, m, l) with
+    l = sum_j exp(s_j - m). A row with no finite entry has P = 0, m = -inf,
+    l = 0.
+    """
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    p = e / l_safe[:, None]
+    return p, m, l
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                   causal: bool, rows=None):
+    """One (sequence, head) of attention: q [Lq, d], k and v [Lk, d].
+
+    Forms S, then P, then O = P V for the selected query rows (all rows if
+    ``rows`` is None), and LSE = m + log(l). Returns (O [R, d], LSE [R]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lq, lk = q.shape[0], k.shape[0]
+    rows = np.arange(lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    if lk == 0 or len(rows) == 0:
+        return out, lse
+    for c0 in range(0, len(rows), ROW_CHUNK):
+        r = rows[c0:c0 + ROW_CHUNK]
+        s = scores(q[r], k, scale)                                # write S
+        s = np.where(visible_mask(r, lk, causal), s, -np.inf)
+        p, m, l = softmax_rows(s)                                 # write P
+        out[c0:c0 + len(r)] = p @ v                               # O = P V
+        with np.errstate(divide="ignore"):
+            lse[c0:c0 + len(r)] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return out, lse
+
+
+def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None):
+    """Full forward pass in the token-major layouts of the module docstring.
+
+    Returns (O, LSE) as float64 arrays.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if cu_seqlens is None:
+        bsz, nq, hq, d = q.shape
+        hkv = k.shape[2]
+        out = np.zeros_like(q)
+        lse = np.full((bsz, hq, nq), -np.inf)
+        for b in range(bsz):
+            for h in range(hq):
+                g = kv_head_of(h, hq, hkv)
+                o_bh, l_bh = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal)
+                out[b, :, h] = o_bh
+                lse[b, h] = l_bh
+        return out, lse
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.zeros_like(q)
+    lse = np.full((hq, t), -np.inf)
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            o_sh, l_sh = attention_head(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], scale, causal)
+            out[lo:hi, h] = o_sh
+            lse[h, lo:hi] = l_sh
+    return out, lse
+
+
+def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None):
+    """Selected outputs only, one (batch-or-sequence, q-head, row) at a time.
+
+    For parity checks at sizes where the full oracle would take too long:
+    each picked row is formed from the definition exactly as in
+    ``attention_ref``. ``picks`` is an int array [P, 3] of (s, h, i) with i
+    local to the sequence. Returns (O [P, d], LSE [P]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    picks = np.asarray(picks, dtype=np.int64).reshape(-1, 3)
+    d = q.shape[-1]
+    out = np.zeros((len(picks), d), dtype=np.float64)
+    lse = np.full(len(picks), -np.inf)
+    if cu_seqlens is None:
+        hq, hkv = q.shape[2], k.shape[2]
+    else:
+        hq, hkv = q.shape[1], k.shape[1]
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+    # group picks by (s, h) so each K/V head slice is upcast once
+    order = np.lexsort((picks[:, 2], picks[:, 1], picks[:, 0]))
+    i0 = 0
+    while i0 < len(order):
+        s, h = picks[order[i0], 0], picks[order[i0], 1]
+        i1 = i0
+        while i1 < len(order) and picks[order[i1], 0] == s and picks[order[i1], 1] == h:
+            i1 += 1
+        sel = order[i0:i1]
+        g = kv_head_of(int(h), hq, hkv)
+        if cu_seqlens is None:
+            qs, ks, vs = q[s, :, h], k[s, :, g], v[s, :, g]
+        else:
+            lo, hi = int(cu[s]), int(cu[s + 1])
+            qs, ks, vs = q[lo:hi, h], k[lo:hi, g], v[lo:hi, g]
+        o_sel, l_sel = attention_head(np.asarray(qs, dtype=np.float64),
+                                      np.asarray(ks, dtype=np.float64),
+                                      np.asarray(vs, dtype=np.float64),
+                                      scale, causal, rows=picks[sel, 2])
+        out[sel] = o_sel
+        lse[sel] = l_sel
+        i0 = i1
+    return out, lse

@@ -1,0 +1,89 @@
+"""Plant plausible mistakes in the oracle and check the pins catch each one.
+
+Every mutant below replaces one step of ``oracle.attention`` (on the CPU,
+through monkeypatch) with a wrong variant: a dropped term, a wrong sign or
+index, a swapped operand. The pin suite must fail for each of them; a mutant
+that every pin lets through would mean the pins do not constrain that step.
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+from oracle_pins import ALL_PINS
+
+_orig_head = A.attention_head
+_orig_softmax = A.softmax_rows
+
+
+def _softmax_no_max(s):
+    e = np.exp(s)
+    l = e.sum(axis=1)
+    with np.errstate(invalid="ignore"):
+        return e / l[:, None], np.zeros(len(s)), l
+
+
+def _softmax_wrong_axis(s):
+    p, m, l = _orig_softmax(s)
+    e = np.exp(s - np.where(np.isfinite(m), m, 0.0)[:, None])
+    col = e.sum(axis=0)
+    return e / np.where(col > 0, col, 1.0)[None, :], m, l
+
+
+def _softmax_lse_no_l(s):
+    p, m, l = _orig_softmax(s)
+    return p, m, np.ones_like(l)
+
+
+def _visible_strict(rows, lk, causal):
+    j = np.arange(lk)[None, :]
+    i = np.asarray(rows)[:, None]
+    return (j < i) if causal else np.broadcast_to(j >= 0, (len(rows), lk))
+
+
+def _visible_reversed(rows, lk, causal):
+    j = np.arange(lk)[None, :]
+    i = np.asarray(rows)[:, None]
+    return (j >= i) if causal else np.broadcast_to(j >= 0, (len(rows), lk))
+
+
+def _visible_ignores_causal(rows, lk, causal):
+    return np.broadcast_to(np.arange(lk)[None, :] >= 0, (len(rows), lk))
+
+
+MUTANTS = {
+    "gqa_modulo_grouping": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "causal_strict_lower": ("visible_mask", _visible_strict),
+    "causal_reversed": ("visible_mask", _visible_reversed),
+    "causal_ignored": ("visible_mask", _visible_ignores_causal),
+    "scale_dropped": ("scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("scores", lambda q, k, scale: (q @ k.T) * scale * scale),
+    "softmax_no_max_shift": ("softmax_rows", _softmax_no_max),
+    "softmax_wrong_axis": ("softmax_rows", _softmax_wrong_axis),
+    "lse_without_denominator": ("softmax_rows", _softmax_lse_no_l),
+    "values_are_keys": ("attention_head",
+                        lambda q, k, v, scale, causal, rows=None: _orig_head(q, k, k, scale, causal, rows)),
+    "lse_log2": ("attention_head",
+                 lambda q, k, v, scale, causal, rows=None:
+                 (lambda o, l: (o, l / np.log(2.0)))(*_orig_head(q, k, v, scale, causal, rows))),
+    "last_key_dropped": ("attention_head",
+                         lambda q, k, v, scale, causal, rows=None:
+                         _orig_head(q, k[:-1], v[:-1], scale, causal, rows)),
+    "first_row_skipped": ("attention_head",
+                          lambda q, k, v, scale, causal, rows=None:
+                          (lambda o, l: (np.concatenate([np.zeros_like(o[:1]), o[1:]]), l))(
+                              *_orig_head(q, k, v, scale, causal, rows))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module draws Q, K, V (and, for packed batches, the sequence lengths)
+from a seeded generator and rounds them to their storage type. It holds no
+attention arithmetic; the oracle and the GPU path both consume what it
+returns, and nothing else is shared between them.
+
+Recipe (identical for every consumer):
+
+* ``rng = numpy.random.default_rng(seed)``, seed ``1000 + workload id`` by
+  default;
+* packed workloads draw the lengths first:
+  ``rng.integers(lo, hi, nseq, endpoint=True)``;
+* then Q, K, V in that order, each ``rng.standard_normal(shape, float32) * sigma``
+  in the token-major layout ([B, N, H, d], or [T, H, d] when packed);
+* bf16 workloads round each float32 value to the nearest bf16, ties to even.
+
+The five workloads are synthetic shapes; none stands for a dataset.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    wid: int
+    name: str
+    dtype: str                 # "fp32" or "bf16" (storage and input type)
+    batch: int                 # B, or the number of packed sequences
+    hq: int
+    hkv: int
+    n: int                     # Nq = Nk for fixed length; unused when packed
+    d: int
+    causal: bool
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    packed_len_range: Optional[tuple] = None   # (lo, hi) inclusive, packed only
+
+    @property
+    def packed(self) -> bool:
+        return self.packed_len_range is not None
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = {
+    1: Workload(1, "fp32 single head, N=256, d=64, non-causal", "fp32",
+                1, 1, 1, 256, 64, False),
+    2: Workload(2, "bf16 16 heads, N=2048, d=64, non-causal", "bf16",
+                1, 16, 16, 2048, 64, False),
+    3: Workload(3, "bf16 causal 32 heads, N=4096, d=128", "bf16",
+                1, 32, 32, 4096, 128, True),
+    4: Workload(4, "bf16 causal GQA 32/8 heads, N=8192, d=128", "bf16",
+                1, 32, 8, 8192, 128, True),
+    5: Workload(5, "bf16 packed causal GQA 32/8, 16 sequences, L~U[128,16384], d=128, "
+                   "Q~N(0,3^2)", "bf16",
+                16, 32, 8, 0, 128, True, sigma_q=3.0, packed_len_range=(128, 16384)),
+}
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even).
+
+    Returns the uint16 bit patterns. Inputs here are finite draws, so no NaN
+    handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Q, K, V as float32 values exactly representable in the storage type,
+    plus the bf16 bit patterns when the storage type is bf16."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dtype: str
+    cu_seqlens: Optional[np.ndarray]      # int32 [nseq + 1] or None
+    lens: Optional[np.ndarray]            # int64 [nseq] or None
+    q_bits: Optional[np.ndarray] = None
+    k_bits: Optional[np.ndarray] = None
+    v_bits: Optional[np.ndarray] = None
+
+    @property
+    def max_seqlen(self) -> int:
+        if self.lens is None:
+            return self.q.shape[1]
+        return int(self.lens.max()) if len(self.lens) else 0
+
+
+def _draw(rng, shape, sigma, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+    if dtype == "bf16":
+        bits = round_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    return x, None
+
+
+def draw(batch: int, hq: int, hkv: int, nq: int, nk: int, d: int, dtype: str,
+         seed: int, sigma=(1.0, 1.0, 1.0), lens=None) -> Inputs:
+    """Draw one input set.
+
+    Fixed length when ``lens`` is None: q [batch, nq, hq, d], k and v
+    [batch, nk, hkv, d]. Packed when ``lens`` is a sequence of lengths (or the
+    tuple ``("uniform", lo, hi)``, drawn first from the same generator):
+    q [T, hq, d], k and v [T, hkv, d], T = sum(lens).
+    """
+    rng = np.random.default_rng(seed)
+    cu = None
+    if lens is not None:
+        if isinstance(lens, tuple) and lens and lens[0] == "uniform":
+            lens = rng.integers(lens[1], lens[2], batch, endpoint=True)
+        lens = np.asarray(lens, dtype=np.int64)
+        cu = np.zeros(len(lens) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lens).astype(np.int32)
+        total = int(cu[-1])
+        qs, ks = (total, hq, d), (total, hkv, d)
+    else:
+        qs, ks = (batch, nq, hq, d), (batch, nk, hkv, d)
+    q, qb = _draw(rng, qs, sigma[0], dtype)
+    k, kb = _draw(rng, ks, sigma[1], dtype)
+    v, vb = _draw(rng, ks, sigma[2], dtype)
+    return Inputs(q, k, v, dtype, cu, lens, qb, kb, vb)
+
+
+def draw_workload(wid: int, seed: Optional[int] = None) -> Inputs:
+    w = WORKLOADS[wid]
+    seed = 1000 + wid if seed is None else seed
+    sig = (w.sigma_q, w.sigma_k, w.sigma_v)
+    if w.packed:
+        lo, hi = w.packed_len_range
+        return draw(w.batch, w.hq, w.hkv, 0, 0, w.d, w.dtype, seed, sig,
+                    lens=("uniform", lo, hi))
+    return draw(w.batch, w.hq, w.hkv, w.n, w.n, w.d, w.dtype, seed, sig)
