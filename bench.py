@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention forward on one MI355X.
+
+A step is one call of ``fa_fwd`` over the whole workload (every query tile
+of every head: score block, mask, online softmax update, P V, epilogue),
+with Q, K, V already resident in HBM when the timed region starts. The
+default workload is causal grouped-query bf16 attention, B=1, Hq=32, Hkv=8,
+N=8192, d=128.
+
+Prints one JSON line with the throughput in TFLOP/s (algorithmic flops:
+4*d per visible query/key pair), the roofline of the kernel (dense bf16
+MFMA bound) and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (bf16, causal, N=8192, d=128) and % of MFMA peak"
+# MI355X published dense peaks (no sparsity): bf16/fp16 MFMA 2.5 PFLOP/s
+# (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s); HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_63_amd", "csrc", "fa_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_causal_gqa_n8192_d128.md")
+
+
+# ---------------------------------------------------------------------------
+# Work and bytes model (host arithmetic, no attention math)
+# ---------------------------------------------------------------------------
+
+def visible_pairs(lq: int, lk: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one head; top-left causal mask."""
+    if not causal:
+        return lq * lk
+    tri = min(lq, lk)
+    return tri * (tri + 1) // 2 + max(0, lq - lk) * lk
+
+
+def algorithmic_flops(lens_q, lens_k, hq: int, d: int, causal: bool) -> int:
+    """4*d flops per visible pair: 2*d for q.k and 2*d for the p*v update."""
+    return sum(4 * d * hq * visible_pairs(a, b, causal) for a, b in zip(lens_q, lens_k))
+
+
+def algorithmic_bytes(tq: int, tk: int, hq: int, hkv: int, d: int, elem: int) -> int:
+    """Compulsory HBM bytes: read Q, K, V once, write O and the fp32 LSE."""
+    return (2 * tq * hq * d + 2 * tk * hkv * d) * elem + 4 * tq * hq
+
+
+def score_matrix_bytes(t_query: int, t_key: int, bytes_per_score: int) -> int:
+    """Dense score-matrix payload of one head: T_query * T_key * s
+    (semiaifoundry "attention-io-tiling", section Score storage)."""
+    return t_query * t_key * bytes_per_score
+
+
+def standard_path_bytes_avoided(lens, hq: int, bytes_per_score: int = 2) -> int:
+    """HBM traffic of the materialising schedule that the tiled kernel never
+    issues: write S, read S, write P, read P (four N x N passes per head)."""
+    return sum(4 * hq * score_matrix_bytes(L, L, bytes_per_score) for L in lens)
+
+
+def workload_lens(inp, w):
+    if inp.lens is not None:
+        return [int(x) for x in inp.lens], [int(x) for x in inp.lens]
+    return [w.n] * w.batch, [w.n] * w.batch
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from committed rocprofv3 counter summaries
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch recorded from FETCH_SIZE/WRITE_SIZE counter runs,
+    or None when no summary exists or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_bytes.group(1))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(inp, w, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole (sequence, head) units of the workload
+    until about ``budget_s`` seconds of CPU work, and scale to TFLOP/s with
+    the same algorithmic flop count as the GPU figure."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    lens_q, lens_k = workload_lens(inp, w)
+    units = [(s, h) for s in range(len(lens_q)) for h in range(w.hq)]
+    # a fixed pseudo-random order so the sample mixes heads and sequences
+    order = np.random.default_rng(7).permutation(len(units))
+    flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    for u in order:
+        s, h = units[u]
+        g = oracle.kv_head_of(h, w.hq, w.hkv)
+        if inp.cu_seqlens is None:
+            qs, ks, vs = inp.q[s, :, h], inp.k[s, :, g], inp.v[s, :, g]
+        else:
+            lo, hi = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
+            qs, ks, vs = inp.q[lo:hi, h], inp.k[lo:hi, g], inp.v[lo:hi, g]
+        oracle.attention_head(qs, ks, vs, w.scale, w.causal)
+        flops += 4 * w.d * visible_pairs(lens_q[s], lens_k[s], w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{done} of {len(units)} (sequence, q-head) units of the same workload, "
+                   f"full rows, fp64 numpy materialising S and P; {dt:.1f} s wall; "
+                   f"BLAS threads {threads}, host cpus {len(os.sched_getaffinity(0))}"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run plain device copies of MIB MiB "
+                         "(calibrates HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the forward pass here has no multi-GPU path "
+              "(no sharding or collectives). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                          "launches": args.steps}))
+        return 0
+
+    import exact_io_aware_63_amd as fa
+
+    w = W.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = W.draw_workload(args.workload)
+    lens_q, lens_k = workload_lens(inp, w)
+    if w.dtype == "bf16":
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+        entry, elem, dtype_name = fa.fa_fwd, 2, "bf16"
+    else:
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+        entry, elem, dtype_name = fa.fa_fwd_fp32, 4, "fp32"
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if inp.cu_seqlens is not None else None
+    o = torch.empty_like(q)
+    if cu is None:
+        B, Nq, Nk = w.batch, w.n, w.n
+        lse = torch.empty((B, w.hq, Nq), dtype=torch.float32, device=dev)
+    else:
+        B, Nq = len(lens_q), inp.max_seqlen
+        Nk = Nq
+        lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    cu_ptr = cu.data_ptr() if cu is not None else None
+
+    def step():
+        st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   B, w.hq, w.hkv, Nq, Nk, w.d, w.scale, int(w.causal), cu_ptr, sptr)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd failed: {fa.fa_status_string(st)}: {fa.fa_last_error()}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K back-to-back launches on the stream they run on, with an
+    # event between consecutive launches for per-launch durations.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    total_ms = events[0].elapsed_time(events[-1])
+
+    ok = bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+
+    flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal)
+    tq, tk = sum(lens_q), sum(lens_k)
+    abytes = algorithmic_bytes(tq, tk, w.hq, w.hkv, w.d, elem)
+    ms_per_step = total_ms / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = float(np.mean(per_launch_ms))
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    if w.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": recorded_traffic() if args.workload == 4 else None}
+    else:
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None}
+
+    line = {
+        "metric": METRIC if args.workload == 4 else f"attention fwd TFLOP/s ({w.name})",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv,
+                   "seq_len": w.n if not w.packed else None,
+                   "seq_lens": lens_q if w.packed else None, "head_dim": w.d,
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": roof,
+        "pct_of_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS if w.dtype == "bf16" else None,
+        "detail": {
+            "alg_flops": flops,
+            "alg_hbm_bytes": abytes,
+            "standard_path_bytes_avoided": standard_path_bytes_avoided(lens_q, w.hq),
+            "launch_ms": {"mean": avg_launch_ms, "min": float(np.min(per_launch_ms)),
+                          "median": float(np.median(per_launch_ms)),
+                          "max": float(np.max(per_launch_ms))},
+            "host_wall_s": wall,
+            "input_gen_s": gen_s,
+            "outputs_finite": ok,
+            "kernel_source_sha256_16": kernel_source_hash(),
+            "device": torch.cuda.get_device_name(dev),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0 if ok else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,150 @@
+"""Python binding of libfa (exact tiled attention forward for MI355X).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
+memory and the stream; the library calls no torch operation.
+
+The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_status_string``,
+``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
+(raw integers and device addresses). ``attention_fwd`` is a convenience
+wrapper that checks torch tensors, allocates O and LSE with torch and calls
+``fa_fwd`` or ``fa_fwd_fp32`` on the current stream.
+
+Importing this package loads ``libfa.so`` from this directory and raises
+ImportError if it is missing: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_UNSUPPORTED = -3
+FA_ERR_ARG = -4
+FA_ERR_HIP = -5
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m exact_io_aware_63_amd.build` "
+        "(hipcc, gfx950). There is no fallback path.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_FWD_ARGS = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+             ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+             ctypes.c_void_p]
+_lib.fa_fwd.argtypes = _FWD_ARGS
+_lib.fa_fwd.restype = ctypes.c_int
+_lib.fa_fwd_fp32.argtypes = _FWD_ARGS
+_lib.fa_fwd_fp32.restype = ctypes.c_int
+_lib.fa_status_string.argtypes = [ctypes.c_int]
+_lib.fa_status_string.restype = ctypes.c_char_p
+_lib.fa_last_error.argtypes = []
+_lib.fa_last_error.restype = ctypes.c_char_p
+_lib.fa_version.argtypes = []
+_lib.fa_version.restype = ctypes.c_int
+
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_status_string", "fa_last_error", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{fa_status_string(status)} ({detail})")
+        self.status = status
+        self.detail = detail
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream) -> int:
+    """C ``fa_fwd``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+                       cu_seqlens, stream)
+
+
+def fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream) -> int:
+    """C ``fa_fwd_fp32``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+                            cu_seqlens, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return _lib.fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return _lib.fa_version()
+
+
+def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
+                  max_seqlen=None, out=None, lse=None, stream=None):
+    """Attention forward on torch device tensors through the C ABI.
+
+    Fixed length: q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d].
+    Packed: q [T, Hq, d], k and v [T, Hkv, d], ``cu_seqlens`` int32 [nseq+1]
+    on the device and ``max_seqlen`` the longest sequence (a host int).
+    bf16 tensors go to ``fa_fwd``, float32 tensors to ``fa_fwd_fp32``.
+    Returns (O, LSE); O has q's shape and dtype, LSE is float32 [B, Hq, Nq]
+    (packed: [Hq, T]).
+    """
+    import torch
+
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dtype == torch.bfloat16:
+        fn = _lib.fa_fwd
+    elif q.dtype == torch.float32:
+        fn = _lib.fa_fwd_fp32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+            raise ValueError("fixed length wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
+        B, Nq, Hq, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("q and k disagree on B or d")
+        lse_shape = (B, Hq, Nq)
+        cu_ptr = None
+    else:
+        if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+            raise ValueError("packed wants q [T,Hq,d], k/v [T,Hkv,d]")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+        if max_seqlen is None:
+            raise ValueError("packed input needs max_seqlen (host int)")
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        if k.shape[0] != T or k.shape[2] != d:
+            raise ValueError("q and k disagree on T or d")
+        B = cu_seqlens.numel() - 1
+        Nq = Nk = int(max_seqlen)
+        lse_shape = (Hq, T)
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cu_ptr, stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return out, lse

@@ -1,0 +1,170 @@
+// C ABI of libfa: argument validation, device check and kernel launch.
+//
+// Every argument check runs on the host before the first HIP call, so the
+// error paths work (and are tested) on machines without a GPU.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kMaxDevices = 64;
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device architecture check, done once per device.
+struct DeviceCheck {
+  std::once_flag once;
+  int status = FA_OK;
+  char msg[256] = "";
+};
+DeviceCheck g_devices[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  DeviceCheck& dc = g_devices[dev];
+  std::call_once(dc.once, [&] {
+    hipDeviceProp_t prop;
+    hipError_t pe = hipGetDeviceProperties(&prop, dev);
+    if (pe != hipSuccess) {
+      dc.status = FA_ERR_HIP;
+      snprintf(dc.msg, sizeof(dc.msg), "hipGetDeviceProperties failed: %s", hipGetErrorString(pe));
+      return;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      dc.status = FA_ERR_UNSUPPORTED;
+      snprintf(dc.msg, sizeof(dc.msg), "device %d is %s; libfa is built for gfx950 only", dev,
+               prop.gcnArchName);
+    }
+  });
+  if (dc.status != FA_OK) return fail(dc.status, "%s", dc.msg);
+  return FA_OK;
+}
+
+// Shared validation for both element types. `elem` is the element size in
+// bytes, `tile_rows` the query rows per workgroup of the kernel.
+int validate(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             const int32_t* cu_seqlens, int tile_rows, bool* noop) {
+  *noop = false;
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B=%d, Nq=%d, Nk=%d must be >= 0", B, Nq, Nk);
+  if (Hq <= 0 || Hkv <= 0)
+    return fail(FA_ERR_SHAPE, "Hq=%d and Hkv=%d must be > 0", Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (cu_seqlens != nullptr && Nq != Nk)
+    return fail(FA_ERR_SHAPE, "packed sequences need Nq == Nk (the maximum length); got %d, %d",
+                Nq, Nk);
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head width d=%d; supported: 64, 128", d);
+  if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
+  if (B == 0 || Nq == 0) {
+    *noop = true;
+    return FA_OK;
+  }
+  if (!Q || !K || !V || !O || !LSE)
+    return fail(FA_ERR_NULL, "Q, K, V, O and LSE must all be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(FA_ERR_ARG, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(LSE, 4) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+    return fail(FA_ERR_ARG, "LSE and cu_seqlens must be 4-byte aligned");
+  const int64_t n_qt = (static_cast<int64_t>(Nq) + tile_rows - 1) / tile_rows;
+  const int64_t grid = n_qt * Hq * static_cast<int64_t>(B);
+  if (grid > 0x7fffffffLL)
+    return fail(FA_ERR_SHAPE, "grid of %lld workgroups exceeds the launch limit",
+                static_cast<long long>(grid));
+  // Element offsets are 64-bit in the kernels; the token counts only need
+  // to fit the int arguments, which they do by type.
+  return FA_OK;
+}
+
+int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+        int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
+        void* stream) {
+  g_last_error[0] = '\0';
+  bool noop = false;
+  const int tile_rows = bf16 ? fa::kBf16TileRows : fa::kFp32TileRows;
+  int st = validate(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, cu_seqlens, tile_rows, &noop);
+  if (st != FA_OK || noop) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.cu_seqlens = cu_seqlens;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.d = d;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.causal = causal ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = bf16 ? fa::launch_fwd_bf16(p, s) : fa::launch_fwd_fp32(p, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq, int Hkv,
+           int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
+           void* stream) {
+  return run(true, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream);
+}
+
+int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O, float* LSE, int B,
+                int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                const int32_t* cu_seqlens, void* stream) {
+  return run(false, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head width or device not supported";
+    case FA_ERR_ARG: return "FA_ERR_ARG: non-finite scale or misaligned pointer";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

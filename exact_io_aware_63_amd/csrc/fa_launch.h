@@ -1,0 +1,40 @@
+// Internal interface between the host entry points (fa_api.cpp) and the
+// device kernels. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fa {
+
+// One attention-forward problem, already validated on the host.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens;  // device pointer, or nullptr for fixed length
+  int batch;                  // B, or number of packed sequences
+  int hq;
+  int hkv;
+  int nq;                     // packed: maximum sequence length
+  int nk;
+  int d;
+  float scale_log2;           // scale * log2(e): scores are kept in base 2
+  int causal;
+};
+
+// Launch the bf16 kernel (d in {64, 128}). Returns the hipError_t of the
+// launch.
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+
+// Launch the float32 kernel (d in {64, 128}).
+hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);
+
+// Query tile height of each kernel (rows of Q per workgroup); the host uses
+// it to bound the grid size.
+constexpr int kBf16TileRows = 128;
+constexpr int kFp32TileRows = 64;
+
+}  // namespace fa

@@ -1,0 +1,119 @@
+/*
+ * libfa: exact tiled scaled-dot-product attention, forward pass, for AMD
+ * Instinct MI355X (gfx950). C ABI.
+ *
+ * The operation ("Softmax does not need the matrix", opening equation and
+ * section "Carry the Normalizer"; "Understanding FlashAttention Pt 1:
+ * Personal Notes", section 0.2 Notation):
+ *
+ *     S = scale * Q K^T,   P = softmax_row(S),   O = P V,
+ *     LSE_i = ln sum_{visible j} exp(S_ij)
+ *
+ * computed exactly (up to floating-point rounding order) without ever
+ * storing S or P: for each query tile the kernel streams K/V blocks through
+ * on-chip memory, updates the running row state (m, l, a) with the
+ * exp(m - m') rescale ("Carry the Normalizer"), and writes only O and the
+ * per-row log-sum-exp ("Understanding FlashAttention Pt 1", section 1.2: a
+ * score tile is computed, used with V_j and discarded; semiaifoundry
+ * "attention-io-tiling", section The mechanism).
+ *
+ * Layout. Every buffer is contiguous, row-major and token-major.
+ *   Fixed length (cu_seqlens == NULL):
+ *     Q [B, Nq, Hq, d]   K, V [B, Nk, Hkv, d]   O [B, Nq, Hq, d]
+ *     LSE [B, Hq, Nq] (float32)
+ *   Packed variable length (cu_seqlens != NULL):
+ *     B is the number of sequences; cu_seqlens is int32 [B + 1] in DEVICE
+ *     memory, cu_seqlens[0] = 0, non-decreasing; sequence s owns tokens
+ *     cu_seqlens[s] .. cu_seqlens[s+1]-1 on both the query and key side
+ *     (self-attention; no attention across sequences).
+ *     Q, O [T, Hq, d]   K, V [T, Hkv, d]   LSE [Hq, T],  T = cu_seqlens[B].
+ *     Nq and Nk must both equal the largest sequence length (it sizes the
+ *     grid); rows of a longer sequence beyond Nq are not written.
+ *
+ * Semantics.
+ *   - scale is applied to Q K^T (the usual value is 1/sqrt(d)).
+ *   - causal != 0 keeps key j for query i iff j <= i (top-left
+ *     lower-triangular, indices local to the batch entry or sequence).
+ *   - Grouped-query attention: Hq % Hkv == 0 and query head h reads K/V
+ *     head h / (Hq / Hkv) (contiguous groups; Hkv == 1 is multi-query).
+ *   - A row that sees no key (Nk == 0, or an empty sequence) gets O = 0 and
+ *     LSE = -inf.
+ *   - fa_fwd: Q, K, V, O are bfloat16 (stored as 16-bit words); scores,
+ *     softmax state and accumulation are float32; P is rounded to bf16 for
+ *     the P V product; O is normalised in float32 and rounded to bf16 once
+ *     (round to nearest even). fa_fwd_fp32: everything float32.
+ *   - Results are exact up to rounding order, not bitwise equal to another
+ *     implementation; repeated calls with the same inputs on the same device
+ *     give bitwise-identical outputs.
+ *
+ * Ownership. The caller allocates every buffer on the current HIP device
+ * and keeps it alive until the work on `stream` completes. The library
+ * allocates no device memory, keeps no pointer after returning, and does
+ * not synchronise. `stream` is a hipStream_t (NULL = the null stream).
+ * Calls are thread-safe.
+ *
+ * Errors. Every function returns a status (FA_OK or a negative FA_ERR_*);
+ * no exception crosses the ABI. All argument checks run on the host before
+ * any HIP call. fa_last_error() gives a thread-local message for the last
+ * failing call on this thread. Device-side faults are asynchronous and
+ * surface at the caller's next synchronisation. The contents of cu_seqlens
+ * live on the device and are not checked: offsets that are decreasing or
+ * exceed the buffers are undefined behaviour.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* B/Hq/Hkv/Nq/Nk inconsistent or out of range */
+  FA_ERR_UNSUPPORTED = -3, /* head width d not in {64, 128}, or not gfx950 */
+  FA_ERR_ARG = -4,         /* scale not finite, or a pointer misaligned */
+  FA_ERR_HIP = -5          /* a HIP runtime call or the launch failed */
+};
+
+/*
+ * Attention forward, bf16 inputs and output, float32 LSE.
+ *   Q, K, V, O : device pointers, bf16, 16-byte aligned, layouts above.
+ *   LSE        : device pointer, float32, 4-byte aligned (required).
+ *   B          : batch size, or number of sequences when packed (B >= 0;
+ *                B == 0 is a no-op).
+ *   Hq, Hkv    : query and K/V head counts, Hq % Hkv == 0.
+ *   Nq, Nk     : query and key lengths (>= 0; Nq == 0 is a no-op); packed:
+ *                both the maximum sequence length.
+ *   d          : head width, 64 or 128.
+ *   scale      : finite float applied to Q K^T.
+ *   causal     : 0 or non-zero (top-left mask, see above).
+ *   cu_seqlens : NULL for fixed length, else device int32 [B + 1].
+ *   stream     : hipStream_t to launch on.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d,
+           float scale, int causal, const int32_t* cu_seqlens, void* stream);
+
+/* Same contract with float32 Q, K, V, O (no bf16 rounding anywhere). */
+int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O,
+                float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, const int32_t* cu_seqlens,
+                void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_io_aware_63_amd as fa
+    return fa
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(
+        ["fa_fwd", "fa_fwd_fp32", "fa_status_string", "fa_last_error", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+    assert set(fa.EXPORTED) == set(_declared_functions())
+
+
+def test_binding_names_match_c_names(fa):
+    for name in _declared_functions():
+        assert callable(getattr(fa, name))
+
+
+def test_version_and_status_strings(fa):
+    assert fa.fa_version() == 10000
+    for st in (0, -1, -2, -3, -4, -5):
+        assert fa.fa_status_string(st)
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert "unknown" in fa.fa_status_string(7)
+
+
+# Fake, 16-byte aligned, never dereferenced addresses: every case below must
+# be rejected before the library touches a pointer or the HIP runtime.
+P = 0x10000
+GOOD = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, scale=0.125,
+            causal=0, cu=None, stream=None)
+
+
+def _call(fa, fn, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+              a["Nk"], a["d"], a["scale"], a["causal"], a["cu"], a["stream"])
+
+
+BAD = [
+    ("null_q", dict(q=0), -1),
+    ("null_k", dict(k=0), -1),
+    ("null_v", dict(v=0), -1),
+    ("null_o", dict(o=0), -1),
+    ("null_lse", dict(lse=0), -1),
+    ("neg_batch", dict(B=-1), -2),
+    ("neg_nq", dict(Nq=-3), -2),
+    ("neg_nk", dict(Nk=-1), -2),
+    ("zero_hq", dict(Hq=0), -2),
+    ("zero_hkv", dict(Hkv=0), -2),
+    ("hq_not_multiple", dict(Hq=6, Hkv=4), -2),
+    ("packed_nq_ne_nk", dict(cu=P, Nq=8, Nk=9), -2),
+    ("d_96", dict(d=96), -3),
+    ("d_256", dict(d=256), -3),
+    ("d_0", dict(d=0), -3),
+    ("scale_nan", dict(scale=math.nan), -4),
+    ("scale_inf", dict(scale=math.inf), -4),
+    ("misaligned_q", dict(q=P + 8), -4),
+    ("misaligned_o", dict(o=P + 2), -4),
+    ("misaligned_lse", dict(lse=P + 2), -4),
+    ("misaligned_cu", dict(cu=P + 2), -4),
+    ("grid_too_large", dict(B=1 << 20, Hq=1 << 10, Hkv=1, Nq=1 << 16, Nk=8), -2),
+]
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])
+@pytest.mark.parametrize("name,kw,status", BAD, ids=[b[0] for b in BAD])
+def test_rejects_bad_arguments(fa, entry, name, kw, status):
+    st = _call(fa, getattr(fa, entry), **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error(), "a failing call must leave a message"
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0),
+                                dict(Nq=0, cu=P, Nk=0)])
+def test_empty_work_is_a_noop(fa, entry, kw):
+    assert _call(fa, getattr(fa, entry), **kw) == 0
+    assert fa.fa_last_error() == ""
+
+
+def test_valid_call_without_gpu_fails_cleanly(fa):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _call(fa, fa.fa_fwd)
+    assert st == fa.FA_ERR_HIP
+    assert "hip" in fa.fa_last_error().lower()
+
+
+def test_attention_fwd_checks_tensors(fa):
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attention_fwd(q, q, q)          # host tensors are refused
+    with pytest.raises(TypeError):
+        fa.attention_fwd(q.half(), q.half(), q.half())
