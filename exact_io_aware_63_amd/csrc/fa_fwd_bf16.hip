@@ -12,16 +12,24 @@
 // Work decomposition (one workgroup = 4 wavefronts of 64 lanes):
 //   * a workgroup owns 128 query rows of one (batch or sequence, q-head);
 //     wavefront w owns rows 32w .. 32w+31 of that tile;
-//   * K/V blocks of 64 keys are staged in LDS and shared by the 4 waves;
+//   * K/V blocks of 64 keys stream through LDS in two stages: while the
+//     waves compute on block j, buffer-to-LDS loads (no VGPR staging) bring
+//     block j+1 into the other stage; rows past the end of the sequence lie
+//     outside the buffer range and arrive as zeros;
 //   * each wave computes the transposed score block S^T = K_j Q_i^T with
-//     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of ONE query row
-//     (its column): row max and row sum are lane-local plus one exchange with
-//     lane ^ 32, and the rescale factor is a per-lane scalar;
-//   * the output is accumulated transposed as well, O^T += V_j^T P^T, so
-//     P^T feeds the B operand straight from the score registers and V^T is
-//     read from LDS, where V is stored transposed with keys permuted to match
-//     the score registers' key order.
+//     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of ONE query row:
+//     row max and row sum are lane-local plus one v_permlane32_swap with the
+//     other half-wave, and the rescale factor is a per-lane scalar;
+//   * the output is accumulated transposed as well, O^T += V_j^T P^T: P^T
+//     feeds the B operand straight from the score registers, and V^T comes
+//     from the row-major V tile through ds_read_b64_tr_b16 transposing reads.
+//   * K/V tiles are stored with an XOR swizzle of the 16-byte units of each
+//     row so that the score reads (16 consecutive rows, same column) and the
+//     transposing V reads (4 consecutive rows, 64 bytes each) spread over the
+//     LDS banks.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "fa_launch.h"
 
@@ -30,57 +38,121 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr int kBR = kBf16TileRows;  // query rows per workgroup
 constexpr int kBC = 64;             // keys per K/V block
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.6931471805599453f;
+// Third descriptor word of a raw buffer resource on gfx9-family parts
+// (32-bit data format, no swizzle); the range check uses num_records.
+constexpr int kBufferFlags = 0x00020000;
 
-__device__ __forceinline__ u32x4 ld16(const u16* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+template <int D>
+struct Tile {
+  static constexpr int kUnits = D / 8;               // 16-byte units per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kBC * kRowBytes;     // one K or V tile
+  static constexpr int kLoads = kBC * kUnits / kThreads;  // loads per lane per tile
+};
+
+// XOR swizzle of the 16-byte unit index within a row.
+template <int UNITS>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (UNITS == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ u32x4 ld16(const u16* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// max and sum of a value with the same lane of the other half-wave
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of key k (0..63 within a block) inside a row of the transposed V
-// tile. Lanes 0-31 of a 32x32x16 score tile hold keys {0-3, 8-11} of every
-// 16-key group and lanes 32-63 hold keys {4-7, 12-15}; storing V^T in that
-// order lets each lane read its 8 keys as one 16-byte LDS load.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int grp = k >> 4, u = k & 15;
-  const int half = (u >> 2) & 1;
-  const int slot = ((u >> 3) << 2) | (u & 3);
-  return (grp << 4) | (half << 3) | slot;
+// Start the loads of one K/V block (keys k0 .. k0+63) into an LDS stage.
+// Each lane moves kLoads 16-byte units of K and of V; a wave instruction
+// fills 1 KiB of contiguous LDS. Rows at or past Lk are outside the buffer
+// range and are written as zeros.
+template <int D>
+__device__ __forceinline__ void issue_block(const u16* kg, const u16* vg, long kstride, int k0,
+                                            int Lk, unsigned char* kdst, unsigned char* vdst,
+                                            int tid, int w) {
+  using T = Tile<D>;
+  const int rows = min(Lk - k0, kBC);
+  const uint32_t kstride_b = static_cast<uint32_t>(kstride * 2);
+  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * kstride_b + T::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(kg + static_cast<long>(k0) * kstride), 0, nrec, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(vg + static_cast<long>(k0) * kstride), 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int it = 0; it < T::kLoads; ++it) {
+    const int u = it * kThreads + tid;
+    const int row = u / T::kUnits;
+    const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
+    const uint32_t voff = row * kstride_b + gc * 16;
+    const int lds_off = (it * kThreads + w * 64) * 16;  // wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + lds_off), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + lds_off), 16, voff, 0, 0, 0);
+  }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p, int n_qt) {
-  constexpr int KSTR = D + 8;    // K tile row stride in LDS (elements)
-  constexpr int VSTR = kBC + 8;  // V^T tile row stride in LDS (elements)
-  constexpr int NC = D / 16;     // 16-wide d chunks of the QK^T contraction
-  constexpr int ND = D / 32;     // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) u16 ks[kBC * KSTR];
-  __shared__ __attribute__((aligned(16))) u16 vt[D * VSTR];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(FwdParams p, int n_qt) {
+  using T = Tile<D>;
+  constexpr int NC = D / 16;  // 16-wide d chunks of the QK^T contraction
+  constexpr int ND = D / 32;  // 32-row tiles of O^T
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int j = lane & 31;   // query column within the wave / key row in A
-  const int h2 = lane >> 5;  // which half of the wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;   // query column of S^T / O^T; key row of the K operand
+  const int h2 = lane >> 5;  // half-wave
 
-  // Heaviest query tiles first: with the causal mask tile t costs ~t+1
-  // blocks, so starting from the last tile shortens the tail.
-  const int bh = p.hq * p.batch;
-  const int tile = n_qt - 1 - static_cast<int>(blockIdx.x / bh);
-  const int rem = static_cast<int>(blockIdx.x % bh);
-  const int b = rem / p.hq;
-  const int h = rem % p.hq;
-  const int kvh = h / (p.hq / p.hkv);
+  // Map the workgroup to (tile, batch-or-sequence, q-head). Workgroup ids are
+  // dealt round-robin to the 8 XCDs (id % 8), each with its own L2. When the
+  // K/V heads (over all batch entries) split evenly over the XCDs, every
+  // query tile that reads K/V head u runs on XCD u % 8, so that head's K/V
+  // stay in one L2. Within an XCD, and in the fallback order, the longest
+  // causal tiles go first and the q-heads sharing a K/V head are adjacent.
+  const int gq = p.hq / p.hkv;
+  const int units = p.batch * p.hkv;
+  int tile, b, h;
+  if ((units & 7) == 0) {
+    const int x = blockIdx.x & 7;
+    const int idx = blockIdx.x >> 3;
+    const int hh = idx % gq;
+    const int t2 = idx / gq;
+    const int upx = units >> 3;
+    const int u = (t2 % upx) * 8 + x;
+    tile = n_qt - 1 - t2 / upx;
+    b = u / p.hkv;
+    h = (u % p.hkv) * gq + hh;
+  } else {
+    const int bh = p.hq * p.batch;
+    tile = n_qt - 1 - static_cast<int>(blockIdx.x / bh);
+    const int rem = static_cast<int>(blockIdx.x % bh);
+    b = rem / p.hq;
+    h = rem % p.hq;
+  }
+  const int kvh = h / gq;
 
   long q_tok0, k_tok0, lse_base;
   int Lq, Lk;
@@ -107,56 +179,43 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p, int n_q
   const u16* kg = static_cast<const u16*>(p.k) + k_tok0 * kstride + static_cast<long>(kvh) * D;
   const u16* vg = static_cast<const u16*>(p.v) + k_tok0 * kstride + static_cast<long>(kvh) * D;
 
+  int kend = Lk;
+  if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
+  const int nblk = (kend + kBC - 1) / kBC;
+  if (nblk > 0) issue_block<D>(kg, vg, kstride, 0, Lk, k_st0, v_st0, tid, w);
+
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + j;     // this lane's query row
+
+  // A negative scale is applied by negating Q (exact in bf16), so that the
+  // base-2 factor c below is >= 0 and max(c*s) = c*max(s).
+  const float c = fabsf(p.scale_log2);
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q fragment, held in registers for the whole key loop: the B operand of
   // S^T = K Q^T (column = query, 8 consecutive d values per lane).
   bf16x8 qf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+  for (int cc = 0; cc < NC; ++cc) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (qrow < Lq) v = ld16(qg + static_cast<long>(qrow) * qstride + 16 * c + 8 * h2);
-    qf[c] = as_bf16x8(v);
+    if (qrow < Lq) v = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2) ^ qflip;
+    qf[cc] = as_bf16x8(v);
   }
-
-  int kend = Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
-  const int nblk = (kend + kBC - 1) / kBC;
 
   f32x16 acc[ND];
 #pragma unroll
   for (int t = 0; t < ND; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;  // running max of x = s * scale * log2(e)
+  float m_run = -INFINITY;  // running max of x = c * s
   float l_run = 0.f;        // this lane's part of the running denominator
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int k0 = blk * kBC;
-    __syncthreads();  // the previous block's LDS reads are done
-    // Stage K (row-major) and V (transposed, permuted) for keys k0..k0+63.
-    // Keys past the end are zero-filled so that masked lanes multiply zeros.
-#pragma unroll
-    for (int c = tid; c < kBC * (D / 8); c += kThreads) {
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int key = k0 + row;
-      u32x4 kv = {0u, 0u, 0u, 0u};
-      u32x4 vv = {0u, 0u, 0u, 0u};
-      if (key < Lk) {
-        kv = ld16(kg + static_cast<long>(key) * kstride + col);
-        vv = ld16(vg + static_cast<long>(key) * kstride + col);
-      }
-      *reinterpret_cast<u32x4*>(&ks[row * KSTR + col]) = kv;
-      const int pos = vt_pos(row);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(col + 2 * e) * VSTR + pos] = static_cast<u16>(vv[e] & 0xFFFFu);
-        vt[(col + 2 * e + 1) * VSTR + pos] = static_cast<u16>(vv[e] >> 16);
-      }
-    }
-    __syncthreads();
-    if (CAUSAL && k0 > wq0 + 31) continue;  // every key is after every row
+  // Per-lane constants of the LDS reads.
+  const int k_row_off = j * T::kRowBytes;            // + kt * 32 rows
+  const int k_swz = swz<T::kUnits>(j);               // same for row j + 32kt
+  const int tr_i = lane & 15;                        // lane within a 16-lane group
+  const int tr_dgrp = (lane >> 4) & 1;               // which 16 d-columns of the 32-row tile
+  const int tr_h = lane >> 5;                        // which 4-key quarter of each 8 keys
 
+  auto block = [&](const unsigned char* ks, const unsigned char* vs, int k0) {
     // S^T for two 32-key tiles: st[kt][r] is the score of key
     // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query qrow.
     f32x16 st[2];
@@ -164,74 +223,114 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdParams p, int n_q
     for (int kt = 0; kt < 2; ++kt) {
       st[kt] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = as_bf16x8(ld16(&ks[(kt * 32 + j) * KSTR + 16 * c + 8 * h2]));
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], st[kt], 0, 0, 0);
+      for (int cc = 0; cc < NC; ++cc) {
+        const int unit = (2 * cc + h2) ^ k_swz;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kt * 32 * T::kRowBytes + k_row_off +
+                                                         unit * 16);
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], st[kt], 0, 0, 0);
       }
     }
 
-    float x[32];
+    // Online softmax update of this block. Only blocks that reach past the
+    // end of the keys or cross the causal diagonal take the masked variant;
+    // it selects on a per-element visibility test, the other has none.
+    auto update = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      // visible iff key <= lim, with key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4)
+      const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
+      auto vis = [&](int kt, int r) { return 32 * kt + 8 * (r >> 2) + (r & 3) <= lim; };
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[kt * 16 + r] = st[kt][r] * p.scale_log2;
-
-    const bool need_mask = (k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0);
-    if (need_mask) {
+        for (int r = 0; r < 16; ++r)
+          mx = fmaxf(mx, MASKED ? (vis(kt, r) ? st[kt][r] : -INFINITY) : st[kt][r]);
+      mx = xhalf_max(mx);
+      const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
+      const float m_new = fmaxf(m_run, mb);
+      // A row that has seen no visible key keeps m = -inf; 0 is used as the
+      // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      m_run = m_new;
+      float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          const bool vis = key < Lk && (!CAUSAL || key <= qrow);
-          if (!vis) x[kt * 16 + r] = -INFINITY;
+          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], c, -m_ref));
+          if (MASKED) e = vis(kt, r) ? e : 0.f;
+          st[kt][r] = e;
+          rs += e;
         }
-    }
+      l_run = l_run * alpha + rs;  // from the unrounded float32 P
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int t = 0; t < ND; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+      }
+    };
+    if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0))
+      update(std::true_type{});
+    else
+      update(std::false_type{});
 
-    float mb = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mb = fmaxf(mb, x[i]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    // A row that has seen no visible key yet keeps m = -inf; use 0 as the
-    // reference so that 2^(-inf - ref) = 0 instead of NaN.
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-      rs += x[i];
-    }
-    l_run = l_run * alpha + rs;  // from the unrounded float32 P
-    m_run = m_new;
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-      for (int t = 0; t < ND; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-    }
-
-    // P^T as the B operand of O^T += V^T P^T: 16-key chunk c takes score
-    // registers 8(c%2) .. 8(c%2)+7 of tile c/2 (keys 16c + {0-3, 8-11} on
-    // lanes 0-31, 16c + {4-7, 12-15} on lanes 32-63; vt_pos matches).
+    // P^T as the B operand of O^T += V^T P^T: 16-key chunk cc takes score
+    // registers 8(cc%2) .. 8(cc%2)+7 of tile cc/2, i.e. keys
+    // 16cc + 8(s/4) + 4*h2 + (s%4) for slot s.
     bf16x8 pb[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) pb[c][s] = static_cast<__bf16>(x[(c >> 1) * 16 + 8 * (c & 1) + s]);
+      for (int s = 0; s < 8; ++s) pb[cc][s] = static_cast<__bf16>(st[cc >> 1][8 * (cc & 1) + s]);
 
+    // V^T A operand for 32 d-rows (tile t) and 16 keys (chunk cc): two
+    // transposing reads give keys 16cc + 8r + 4*tr_h + (0..3), r = 0, 1, at
+    // d column 32t + 16*tr_dgrp + tr_i. Lane tr_i of each 16-lane group
+    // supplies the address of 4 consecutive d values of key row
+    // (16cc + 8r + 4*tr_h + tr_i/4).
 #pragma unroll
     for (int t = 0; t < ND; ++t)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = as_bf16x8(ld16(&vt[(32 * t + j) * VSTR + 16 * c + 8 * h2]));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[t], 0, 0, 0);
+      for (int cc = 0; cc < 4; ++cc) {
+        s16x4 half[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 16 * cc + 8 * r + 4 * tr_h + (tr_i >> 2);
+          const int unit = (4 * t + 2 * tr_dgrp + ((tr_i & 3) >> 1)) ^ swz<T::kUnits>(row);
+          const int off = row * T::kRowBytes + unit * 16 + (tr_i & 1) * 8;
+          half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + off));
+        }
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], acc[t], 0, 0, 0);
       }
+  };
+
+  // Two-stage pipeline, unrolled by two so that every LDS address has a
+  // fixed stage: wait for this block's loads (own wave), barrier (all waves'
+  // loads landed and the other stage is no longer read), start the next
+  // block's loads into the other stage, compute.
+  for (int blk = 0; blk < nblk; blk += 2) {
+    {
+      const int k0 = blk * kBC;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (blk + 1 < nblk) issue_block<D>(kg, vg, kstride, k0 + kBC, Lk, k_st1, v_st1, tid, w);
+      if (!(CAUSAL && k0 > wq0 + 31)) block(k_st0, v_st0, k0);
+    }
+    if (blk + 1 < nblk) {
+      const int k0 = (blk + 1) * kBC;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (blk + 2 < nblk) issue_block<D>(kg, vg, kstride, k0 + kBC, Lk, k_st0, v_st0, tid, w);
+      if (!(CAUSAL && k0 > wq0 + 31)) block(k_st1, v_st1, k0);
+    }
   }
 
   // Epilogue: o = a / l, rounded once to bf16; LSE = ln(2) * (m + log2 l).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   if (qrow < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     u16* og = static_cast<u16*>(p.o) + (q_tok0 + qrow) * qstride + static_cast<long>(h) * D;

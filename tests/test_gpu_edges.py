@@ -80,6 +80,20 @@ def test_causal_zero_scale_prefix_means(dtype):
     assert max_err(lse, np.broadcast_to(np.log(np.arange(1, n + 1)), lse.shape)) <= 1e-4
 
 
+def _scale_with_power_of_two_factor(min_factor):
+    """A float32 scale whose base-2 factor c = fp32(fp64(scale) * log2 e) is a
+    power of two >= min_factor. With such a c every product c * s is exact
+    in float32, so the weight of a row's maximum is exactly 2^0 = 1."""
+    k = math.ceil(math.log2(min_factor))
+    target = np.float32(2.0 ** k)
+    s0 = np.float32(2.0 ** k / math.log2(math.e))
+    for cand in (s0, np.nextafter(s0, np.float32(np.inf)), np.nextafter(s0, np.float32(0))):
+        c = np.float32(np.float64(cand) * 1.4426950408889634)
+        if c == target:
+            return float(cand)
+    raise AssertionError("no float32 scale with a power-of-two base-2 factor")
+
+
 def test_hard_max_limit_exact():
     """When the top score beats the runner-up by >= 200 in base-2 units, all
     other weights underflow to 0 and O is v_argmax exactly (bf16)."""
@@ -91,7 +105,7 @@ def test_hard_max_limit_exact():
     gap = srt[:, -1] - srt[:, -2]
     keep = gap > 0.05                                        # clear winners only
     assert keep.sum() > 100
-    scale = 200.0 / (gap[keep].min() * math.log2(math.e))
+    scale = _scale_with_power_of_two_factor(200.0 / gap[keep].min())
     o, _ = run_gpu(inp, False, scale)
     arg = s.argmax(axis=1)
     got = o[0, keep, 0]
