@@ -27,8 +27,18 @@
 //     row so that the score reads (16 consecutive rows, same column) and the
 //     transposing V reads (4 consecutive rows, 64 bytes each) spread over the
 //     LDS banks.
+//
+// Reference point of the exponentials. The invariant of "Carry the
+// Normalizer" holds for ANY common reference m of l and a: o = a / l and
+// LSE = m + log l do not depend on it, as long as nothing overflows. The
+// kernel raises m to the new block maximum only when some row of the wave
+// would otherwise see a weight above 2^kLazy; otherwise it keeps m. Each
+// row's first block sets m, so every weight stays below 2^kLazy (far inside
+// the float32 range), and the accumulator rescale, which costs one multiply
+// per accumulator register, becomes rare.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <type_traits>
 
 #include "fa_launch.h"
@@ -49,6 +59,7 @@ constexpr int kBR = kBf16TileRows;  // query rows per workgroup
 constexpr int kBC = 64;             // keys per K/V block
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;        // keep m while the block max is <= m + 8
 // Third descriptor word of a raw buffer resource on gfx9-family parts
 // (32-bit data format, no swizzle); the range check uses num_records.
 constexpr int kBufferFlags = 0x00020000;
@@ -189,7 +200,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
 
   // A negative scale is applied by negating Q (exact in bf16), so that the
   // base-2 factor c below is >= 0 and max(c*s) = c*max(s).
-  const float c = fabsf(p.scale_log2);
+  const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q fragment, held in registers for the whole key loop: the B operand of
@@ -236,18 +247,26 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     // it selects on a per-element visibility test, the other has none.
     auto update = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      // visible iff key <= lim, with key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4)
-      const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
-      auto vis = [&](int kt, int r) { return 32 * kt + 8 * (r >> 2) + (r & 3) <= lim; };
-      float mx = -INFINITY;
+      if (MASKED) {
+        // visible iff key <= lim, with key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4);
+        // c >= FLT_MIN keeps 2^(c * -inf - m) = 0 for the masked entries
+        const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mx = fmaxf(mx, MASKED ? (vis(kt, r) ? st[kt][r] : -INFINITY) : st[kt][r]);
-      mx = xhalf_max(mx);
-      const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const float m_new = fmaxf(m_run, mb);
+          for (int r = 0; r < 16; ++r)
+            st[kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? st[kt][r] : -INFINITY;
+      }
+      float mx = fmaxf(st[0][0], st[0][1]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, st[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[1][r]);
+      const float mb = xhalf_max(mx) * c;
+      // The reference point moves only when some row of the wave gains more
+      // than kLazy over it (wave-uniform decision).
+      const bool raise = __any(mb > m_run + kLazy);
+      const float m_new = raise ? fmaxf(m_run, mb) : m_run;
       // A row that has seen no visible key keeps m = -inf; 0 is used as the
       // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -258,13 +277,11 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], c, -m_ref));
-          if (MASKED) e = vis(kt, r) ? e : 0.f;
-          st[kt][r] = e;
-          rs += e;
+          st[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], c, -m_ref));
+          rs += st[kt][r];
         }
       l_run = l_run * alpha + rs;  // from the unrounded float32 P
-      if (!__all(alpha == 1.f)) {
+      if (raise) {
 #pragma unroll
         for (int t = 0; t < ND; ++t)
 #pragma unroll
