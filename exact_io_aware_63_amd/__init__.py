@@ -31,7 +31,7 @@ FA_ERR_HIP = -5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m exact_io_aware_63_amd.build` "
+        f"{LIB_PATH} is not built; run `python exact_io_aware_63_amd/build.py` "
         "(hipcc, gfx950). There is no fallback path.")
 
 _lib = ctypes.CDLL(LIB_PATH)

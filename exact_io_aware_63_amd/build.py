@@ -1,6 +1,7 @@
 """Build libfa.so in-tree with hipcc for gfx950.
 
-Run ``python -m exact_io_aware_63_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python exact_io_aware_63_amd/build.py`` (or ``__graft_entry__.build()``).
+It imports nothing from the package, so it runs before libfa.so exists.
 """
 from __future__ import annotations
 
