@@ -40,6 +40,7 @@
 
 #include <cfloat>
 #include <type_traits>
+#include <utility>
 
 #include "fa_launch.h"
 
@@ -92,31 +93,74 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Start the loads of one K/V block (keys k0 .. k0+63) into an LDS stage.
-// Each lane moves kLoads 16-byte units of K and of V; a wave instruction
-// fills 1 KiB of contiguous LDS. Rows at or past Lk are outside the buffer
-// range and are written as zeros.
+// Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Instruction plan of one key block for one wave. The block has M matrix
+// steps: 2*NC score MFMAs of the NEXT block (two 32-key tiles x NC d-chunks)
+// and 4*ND P V MFMAs of THIS block (four 16-key chunks x ND d-tiles). The 32
+// exponentials of this block (one per score register of the lane) are
+// spread evenly over the first M - ND steps; P V chunk g is placed right
+// after the step that finishes its 8 probabilities, and score MFMAs fill the
+// remaining steps.
 template <int D>
-__device__ __forceinline__ void issue_block(const u16* kg, const u16* vg, long kstride, int k0,
-                                            int Lk, unsigned char* kdst, unsigned char* vdst,
-                                            int tid, int w) {
+struct Plan {
+  static constexpr int NC = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int M = 2 * NC + 4 * ND;
+  static constexpr int VS = M - ND;  // steps that carry exponentials
+  static constexpr int elem_step(int e) { return e * VS / 32; }
+  static constexpr int pv_start(int g) { return elem_step(8 * g + 7) + 1; }
+  // -1 if step s is a score MFMA, else the P V chunk it belongs to
+  static constexpr int pv_chunk(int s) {
+    for (int g = 0; g < 4; ++g)
+      if (s >= pv_start(g) && s < pv_start(g) + ND) return g;
+    return -1;
+  }
+  // index of the score MFMA at step s (number of score steps before it)
+  static constexpr int qk_index(int s) {
+    int n = 0;
+    for (int i = 0; i < s; ++i) n += pv_chunk(i) < 0 ? 1 : 0;
+    return n;
+  }
+  static constexpr bool valid() {
+    int qk = 0;
+    for (int s = 0; s < M; ++s) qk += pv_chunk(s) < 0 ? 1 : 0;
+    for (int g = 0; g + 1 < 4; ++g)
+      if (pv_start(g + 1) < pv_start(g) + ND) return false;
+    return qk == 2 * NC && pv_start(3) + ND == M;
+  }
+};
+static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
+
+// Start the loads of one 64-key tile of K or V (keys k0 .. k0+63) into LDS.
+// Each lane moves kLoads 16-byte units; a wave instruction fills 1 KiB of
+// contiguous LDS. Rows at or past Lk are outside the buffer range and are
+// written as zeros.
+template <int D>
+__device__ __forceinline__ void issue_tile(const u16* g, long stride, int k0, int Lk,
+                                           unsigned char* dst, int tid, int w) {
   using T = Tile<D>;
   const int rows = min(Lk - k0, kBC);
-  const uint32_t kstride_b = static_cast<uint32_t>(kstride * 2);
-  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * kstride_b + T::kRowBytes;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(kg + static_cast<long>(k0) * kstride), 0, nrec, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(vg + static_cast<long>(k0) * kstride), 0, nrec, kBufferFlags);
+  const uint32_t stride_b = static_cast<uint32_t>(stride * 2);
+  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g + static_cast<long>(k0) * stride), 0, nrec, kBufferFlags);
 #pragma unroll
   for (int it = 0; it < T::kLoads; ++it) {
     const int u = it * kThreads + tid;
     const int row = u / T::kUnits;
     const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
-    const uint32_t voff = row * kstride_b + gc * 16;
+    const uint32_t voff = row * stride_b + gc * 16;
     const int lds_off = (it * kThreads + w * 64) * 16;  // wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + lds_off), 16, voff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + lds_off), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + lds_off), 16, voff, 0, 0, 0);
   }
 }
 
@@ -126,10 +170,12 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   using T = Tile<D>;
   constexpr int NC = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int ND = D / 32;  // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[T::kBytes];
+  // K runs one block ahead of V: block j's scores are formed while block
+  // j-1's probabilities meet V, so each tensor has its own two buffers.
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,7 +239,11 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   int kend = Lk;
   if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
   const int nblk = (kend + kBC - 1) / kBC;
-  if (nblk > 0) issue_block<D>(kg, vg, kstride, 0, Lk, k_st0, v_st0, tid, w);
+  if (nblk > 0) {
+    issue_tile<D>(kg, kstride, 0, Lk, kb0, tid, w);
+    issue_tile<D>(vg, kstride, 0, Lk, vb0, tid, w);
+    if (nblk > 1) issue_tile<D>(kg, kstride, kBC, Lk, kb1, tid, w);
+  }
 
   const int wq0 = q0 + 32 * w;  // first query row of this wave
   const int qrow = wq0 + j;     // this lane's query row
@@ -216,7 +266,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   f32x16 acc[ND];
 #pragma unroll
   for (int t = 0; t < ND; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;  // running max of x = c * s
+  float m_run = -INFINITY;  // running reference of x = c * s
   float l_run = 0.f;        // this lane's part of the running denominator
 
   // Per-lane constants of the LDS reads.
@@ -226,124 +276,152 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   const int tr_dgrp = (lane >> 4) & 1;               // which 16 d-columns of the 32-row tile
   const int tr_h = lane >> 5;                        // which 4-key quarter of each 8 keys
 
-  auto block = [&](const unsigned char* ks, const unsigned char* vs, int k0) {
-    // S^T for two 32-key tiles: st[kt][r] is the score of key
-    // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query qrow.
-    f32x16 st[2];
+  // K operand of S^T = K_j Q^T: 32 key rows (tile kt) x 16 d values (chunk cc).
+  auto k_operand = [&](const unsigned char* ks, int kt, int cc) {
+    const int unit = (2 * cc + h2) ^ k_swz;
+    return *reinterpret_cast<const bf16x8*>(ks + kt * 32 * T::kRowBytes + k_row_off + unit * 16);
+  };
+  // V^T A operand for 32 d-rows (tile t) and 16 keys (chunk cc): two
+  // transposing reads give keys 16cc + 8r + 4*tr_h + (0..3), r = 0, 1, at
+  // d column 32t + 16*tr_dgrp + tr_i. Lane tr_i of each 16-lane group
+  // supplies the address of 4 consecutive d values of key row
+  // (16cc + 8r + 4*tr_h + tr_i/4).
+  auto v_operand = [&](const unsigned char* vs, int t, int cc) {
+    s16x4 half[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 16 * cc + 8 * r + 4 * tr_h + (tr_i >> 2);
+      const int unit = (4 * t + 2 * tr_dgrp + ((tr_i & 3) >> 1)) ^ swz<T::kUnits>(row);
+      const int off = row * T::kRowBytes + unit * 16 + (tr_i & 1) * 8;
+      half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + off));
+    }
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // S^T for two 32-key tiles of one block: s[kt][r] is the score of key
+  // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query qrow.
+  f32x16 sa[2], sb[2];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nblk > 0) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x16{};
+      sa[kt] = f32x16{};
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const int unit = (2 * cc + h2) ^ k_swz;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kt * 32 * T::kRowBytes + k_row_off +
-                                                         unit * 16);
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], st[kt], 0, 0, 0);
-      }
+      for (int cc = 0; cc < NC; ++cc)
+        sa[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kb0, kt, cc), qf[cc], sa[kt],
+                                                         0, 0, 0);
     }
+  }
 
-    // Online softmax update of this block. Only blocks that reach past the
-    // end of the keys or cross the causal diagonal take the masked variant;
-    // it selects on a per-element visibility test, the other has none.
-    auto update = [&](auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      if (MASKED) {
-        // visible iff key <= lim, with key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4);
-        // c >= FLT_MIN keeps 2^(c * -inf - m) = 0 for the masked entries
-        const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st[kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? st[kt][r] : -INFINITY;
+  // One key block j: its scores sc are in registers. On entry the loads of
+  // K_{j+1} and V_j are in flight (issued one block earlier).
+  //   1. wait for them, barrier (every wave is done with block j-1, so the
+  //      buffers of K_j and V_{j-1} are free), start the loads of K_{j+2}
+  //      and V_{j+1} into those buffers;
+  //   2. mask, row maximum, reference update (rare rescale);
+  //   3. the M steps of Plan<D>: the scores of block j+1 (sn) from K_{j+1},
+  //      the exponentials of block j, and O^T += V_j^T P_j^T, one MFMA per
+  //      step, so the matrix cores run while the vector unit computes
+  //      exponentials. Operands are read from LDS kAhead steps early.
+  using PL = Plan<D>;
+  constexpr int kAhead = 2;
+  auto iter = [&](auto par_tag, int jb, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int PAR = decltype(par_tag)::value;  // jb & 1
+    unsigned char* k_next = PAR ? kb0 : kb1;        // K_{j+1}
+    unsigned char* k_free = PAR ? kb1 : kb0;        // K_j, consumed
+    unsigned char* v_cur = PAR ? vb1 : vb0;         // V_j
+    unsigned char* v_free = PAR ? vb0 : vb1;        // V_{j-1}, consumed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (jb + 2 < nblk) issue_tile<D>(kg, kstride, (jb + 2) * kBC, Lk, k_free, tid, w);
+    if (jb + 1 < nblk) issue_tile<D>(vg, kstride, (jb + 1) * kBC, Lk, v_free, tid, w);
+    const int k0 = jb * kBC;
+
+    bf16x8 opnd[PL::M];
+    auto load_operand = [&](auto S) {
+      constexpr int g = PL::pv_chunk(S);
+      if constexpr (g < 0) {
+        constexpr int q = PL::qk_index(S);
+        opnd[S] = k_operand(k_next, q & 1, q >> 1);
+      } else {
+        opnd[S] = v_operand(v_cur, S - PL::pv_start(g), g);
       }
-      float mx = fmaxf(st[0][0], st[0][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, st[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[1][r]);
-      const float mb = xhalf_max(mx) * c;
-      // The reference point moves only when some row of the wave gains more
-      // than kLazy over it (wave-uniform decision).
-      const bool raise = __any(mb > m_run + kLazy);
-      const float m_new = raise ? fmaxf(m_run, mb) : m_run;
-      // A row that has seen no visible key keeps m = -inf; 0 is used as the
-      // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      m_run = m_new;
-      float rs = 0.f;
+    };
+    static_for<kAhead>(load_operand);
+
+    // Only blocks that reach past the end of the keys or cross the causal
+    // diagonal are masked: visible iff key <= lim, with key - k0 - 4*h2 =
+    // 32kt + 8(r/4) + (r%4). c >= FLT_MIN keeps 2^(c * -inf - m) = 0.
+    if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0)) {
+      const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          st[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], c, -m_ref));
-          rs += st[kt][r];
-        }
-      l_run = l_run * alpha + rs;  // from the unrounded float32 P
-      if (raise) {
+        for (int r = 0; r < 16; ++r)
+          sc[kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[kt][r] : -INFINITY;
+    }
+    float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-        for (int t = 0; t < ND; ++t)
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-      }
-    };
-    if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0))
-      update(std::true_type{});
-    else
-      update(std::false_type{});
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    const float mb = xhalf_max(mx) * c;
+    // The reference point moves only when some row of the wave gains more
+    // than kLazy over it (wave-uniform decision).
+    const bool raise = __any(mb > m_run + kLazy);
+    if (raise) {
+      const float m_new = fmaxf(m_run, mb);
+      // A row that has seen no visible key keeps m = -inf; 0 is used as the
+      // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < ND; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    }
+    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
 
-    // P^T as the B operand of O^T += V^T P^T: 16-key chunk cc takes score
-    // registers 8(cc%2) .. 8(cc%2)+7 of tile cc/2, i.e. keys
-    // 16cc + 8(s/4) + 4*h2 + (s%4) for slot s.
+    // P^T as the B operand of O^T += V^T P^T: 16-key chunk g takes score
+    // registers 8(g%2) .. 8(g%2)+7 of tile g/2, i.e. keys
+    // 16g + 8(s/4) + 4*h2 + (s%4) for slot s.
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pb[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pb[cc][s] = static_cast<__bf16>(st[cc >> 1][8 * (cc & 1) + s]);
-
-    // V^T A operand for 32 d-rows (tile t) and 16 keys (chunk cc): two
-    // transposing reads give keys 16cc + 8r + 4*tr_h + (0..3), r = 0, 1, at
-    // d column 32t + 16*tr_dgrp + tr_i. Lane tr_i of each 16-lane group
-    // supplies the address of 4 consecutive d values of key row
-    // (16cc + 8r + 4*tr_h + tr_i/4).
-#pragma unroll
-    for (int t = 0; t < ND; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        s16x4 half[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * cc + 8 * r + 4 * tr_h + (tr_i >> 2);
-          const int unit = (4 * t + 2 * tr_dgrp + ((tr_i & 3) >> 1)) ^ swz<T::kUnits>(row);
-          const int off = row * T::kRowBytes + unit * 16 + (tr_i & 1) * 8;
-          half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + off));
-        }
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], acc[t], 0, 0, 0);
+    static_for<PL::M>([&](auto S) {
+      if constexpr (S + kAhead < PL::M) load_operand(std::integral_constant<int, S + kAhead>{});
+      constexpr int g = PL::pv_chunk(S);
+      if constexpr (g < 0) {
+        constexpr int q = PL::qk_index(S);
+        constexpr int kt = q & 1, cc = q >> 1;
+        sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[S], qf[cc],
+                                                         cc == 0 ? f32x16{} : sn[kt], 0, 0, 0);
+      } else {
+        constexpr int t = S - PL::pv_start(g);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[S], pb[g], acc[t], 0, 0, 0);
       }
+      static_for<32>([&](auto E) {
+        if constexpr (PL::elem_step(E) == S) {
+          constexpr int eg = E / 8, es = E % 8;
+          const float x = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[eg >> 1][8 * (eg & 1) + es], c, -m_ref));
+          rs[eg] += x;
+          pb[eg][es] = static_cast<__bf16>(x);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);  // from the unrounded float32 P
   };
 
-  // Two-stage pipeline, unrolled by two so that every LDS address has a
-  // fixed stage: wait for this block's loads (own wave), barrier (all waves'
-  // loads landed and the other stage is no longer read), start the next
-  // block's loads into the other stage, compute.
-  for (int blk = 0; blk < nblk; blk += 2) {
-    {
-      const int k0 = blk * kBC;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (blk + 1 < nblk) issue_block<D>(kg, vg, kstride, k0 + kBC, Lk, k_st1, v_st1, tid, w);
-      if (!(CAUSAL && k0 > wq0 + 31)) block(k_st0, v_st0, k0);
-    }
-    if (blk + 1 < nblk) {
-      const int k0 = (blk + 1) * kBC;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (blk + 2 < nblk) issue_block<D>(kg, vg, kstride, k0 + kBC, Lk, k_st0, v_st0, tid, w);
-      if (!(CAUSAL && k0 > wq0 + 31)) block(k_st1, v_st1, k0);
-    }
+  // The last block also forms the scores of a block past the end (from the
+  // stale K buffer, discarded): one branch-free loop body for every block.
+  for (int jb = 0; jb < nblk; jb += 2) {
+    iter(std::integral_constant<int, 0>{}, jb, sa, sb);
+    if (jb + 1 >= nblk) break;
+    iter(std::integral_constant<int, 1>{}, jb + 1, sb, sa);
   }
 
   // Epilogue: o = a / l, rounded once to bf16; LSE = ln(2) * (m + log2 l).
