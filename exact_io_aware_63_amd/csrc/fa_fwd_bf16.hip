@@ -9,20 +9,26 @@
 // sum e^(s-m') v). Scores are kept in base 2: x = s * scale * log2(e), so
 // every exponential is one v_exp_f32 and e^(m-m') becomes 2^(m-m').
 //
-// Work decomposition (one workgroup = 4 wavefronts of 64 lanes):
-//   * a workgroup owns 128 query rows of one (batch or sequence, q-head);
-//     wavefront w owns rows 32w .. 32w+31 of that tile;
-//   * K/V blocks of 64 keys stream through LDS in two stages: while the
-//     waves compute on block j, buffer-to-LDS loads (no VGPR staging) bring
-//     block j+1 into the other stage; rows past the end of the sequence lie
-//     outside the buffer range and arrive as zeros;
+// Work decomposition (one workgroup = 4 wavefronts of 64 lanes, one
+// wavefront per SIMD, so each wavefront has the whole register file):
+//   * a workgroup owns 256 query rows of one (batch or sequence, q-head);
+//     wavefront w owns rows 64w .. 64w+63 of that tile as two 32-row query
+//     tiles, so every K or V operand read from LDS feeds two MFMAs;
+//   * K/V blocks of 64 keys stream through LDS with buffer-to-LDS loads (no
+//     VGPR staging); K runs one block ahead of V, each with two buffers;
+//     rows past the end of the sequence lie outside the buffer range and
+//     arrive as zeros;
 //   * each wave computes the transposed score block S^T = K_j Q_i^T with
-//     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of ONE query row:
-//     row max and row sum are lane-local plus one v_permlane32_swap with the
-//     other half-wave, and the rescale factor is a per-lane scalar;
+//     v_mfma_f32_32x32x16_bf16, so a lane holds 32 scores of ONE query row
+//     per query tile: row max and row sum are lane-local plus one
+//     v_permlane32_swap with the other half-wave, and the rescale factor is
+//     a per-lane scalar;
 //   * the output is accumulated transposed as well, O^T += V_j^T P^T: P^T
 //     feeds the B operand straight from the score registers, and V^T comes
-//     from the row-major V tile through ds_read_b64_tr_b16 transposing reads.
+//     from the row-major V tile through ds_read_b64_tr_b16 transposing reads;
+//   * the key loop is software-pipelined: while the exponentials of block j
+//     are computed, the matrix cores form the scores of block j+1 and
+//     accumulate P_j V_j, in a fixed compile-time interleave (Plan);
 //   * K/V tiles are stored with an XOR swizzle of the 16-byte units of each
 //     row so that the score reads (16 consecutive rows, same column) and the
 //     transposing V reads (4 consecutive rows, 64 bytes each) spread over the
@@ -30,12 +36,13 @@
 //
 // Reference point of the exponentials. The invariant of "Carry the
 // Normalizer" holds for ANY common reference m of l and a: o = a / l and
-// LSE = m + log l do not depend on it, as long as nothing overflows. The
-// kernel raises m to the new block maximum only when some row of the wave
-// would otherwise see a weight above 2^kLazy; otherwise it keeps m. Each
-// row's first block sets m, so every weight stays below 2^kLazy (far inside
-// the float32 range), and the accumulator rescale, which costs one multiply
-// per accumulator register, becomes rare.
+// LSE = m + log l do not depend on it, as long as nothing overflows. A row's
+// first visible block sets m (its accumulator is still zero, so nothing is
+// rescaled); afterwards m is kept while the weights stay below 2^kRaise.
+// Only when some row of a wave would exceed that are the wave's references
+// raised to the block maxima and the accumulators rescaled, a path realistic
+// inputs rarely take; it passes the accumulator through private memory so
+// that the vector unit never reads it and it stays in AGPRs.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -60,7 +67,7 @@ constexpr int kBR = kBf16TileRows;  // query rows per workgroup
 constexpr int kBC = 64;             // keys per K/V block
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;        // keep m while the block max is <= m + 8
+constexpr float kRaise = 16.f;      // the main loop keeps m while the block max is <= m + 16
 // Third descriptor word of a raw buffer resource on gfx9-family parts
 // (32-bit data format, no swizzle); the range check uses num_records.
 constexpr int kBufferFlags = 0x00020000;
@@ -93,6 +100,55 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Score MFMA (S^T tile = K operand x Q fragment), written as inline asm so
+// that the score accumulator is a VGPR (the vector unit reads it next) while
+// the Q fragment stays in an AGPR (only the matrix cores read it). The
+// compiler does not see these as MFMAs: the dependent vector reads of a
+// score tile are kept at least 19 wait states after its last MFMA by the
+// instruction plan and by explicit s_nop guards.
+__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// 21 wait states: covers a 16-pass MFMA result before a dependent read.
+__device__ __forceinline__ void mfma_result_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Read an accumulator tile held in AGPRs into VGPRs (explicit moves, so
+// that the compiler keeps the tile itself in AGPRs).
+__device__ __forceinline__ f32x16 read_agpr(f32x16 a) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[i]));
+    r[i] = x;
+  }
+  return r;
+}
+
+// Multiply an accumulator tile that lives in AGPRs by a per-lane factor,
+// passing it through private memory: memory instructions take AGPR data
+// directly, so no vector instruction reads the tile and the compiler keeps
+// it in AGPRs everywhere else. Used only on the rare rescale path.
+__device__ __forceinline__ f32x16 scale_via_scratch(f32x16 a, float f) {
+  volatile f32x16 tmp;
+  tmp = a;
+  f32x16 x = tmp;
+  x *= f;
+  tmp = x;
+  f32x16 r = tmp;
+  asm volatile("" : "+a"(r));
+  return r;
+}
+
 // Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -103,25 +159,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Instruction plan of one key block for one wave. The block has M matrix
-// steps: 2*NC score MFMAs of the NEXT block (two 32-key tiles x NC d-chunks)
-// and 4*ND P V MFMAs of THIS block (four 16-key chunks x ND d-tiles). The 32
-// exponentials of this block (one per score register of the lane) are
-// spread evenly over the first M - ND steps; P V chunk g is placed right
-// after the step that finishes its 8 probabilities, and score MFMAs fill the
+// Instruction plan of one key block for one wave (two 32-row query tiles).
+// The block has M matrix steps: 4*NC score MFMAs of the NEXT block (two
+// 32-key tiles x NC d-chunks x two query tiles) and 8*ND P V MFMAs of THIS
+// block (four 16-key chunks x ND d-tiles x two query tiles). Consecutive
+// steps share one LDS operand (the two query tiles). The 64 exponentials of
+// this block (32 score registers per query tile) are spread evenly over the
+// first M - 2*ND steps; P V chunk g is placed right after the step that
+// finishes its 16 probabilities (8 per query tile), and score MFMAs fill the
 // remaining steps.
 template <int D>
 struct Plan {
   static constexpr int NC = D / 16;
   static constexpr int ND = D / 32;
-  static constexpr int M = 2 * NC + 4 * ND;
-  static constexpr int VS = M - ND;  // steps that carry exponentials
-  static constexpr int elem_step(int e) { return e * VS / 32; }
-  static constexpr int pv_start(int g) { return elem_step(8 * g + 7) + 1; }
+  static constexpr int M = 4 * NC + 8 * ND;
+  static constexpr int VS = M - 2 * ND;  // steps that carry exponentials
+  static constexpr int elem_step(int e) { return e * VS / 64; }
+  // elements of step s: first_elem(s) .. first_elem(s + 1) - 1
+  static constexpr int first_elem(int s) { return (s * 64 + VS - 1) / VS; }
+  static constexpr int pv_start(int g) { return elem_step(16 * g + 15) + 1; }
   // -1 if step s is a score MFMA, else the P V chunk it belongs to
   static constexpr int pv_chunk(int s) {
     for (int g = 0; g < 4; ++g)
-      if (s >= pv_start(g) && s < pv_start(g) + ND) return g;
+      if (s >= pv_start(g) && s < pv_start(g) + 2 * ND) return g;
     return -1;
   }
   // index of the score MFMA at step s (number of score steps before it)
@@ -130,12 +190,22 @@ struct Plan {
     for (int i = 0; i < s; ++i) n += pv_chunk(i) < 0 ? 1 : 0;
     return n;
   }
+  // Score MFMA q: key tile q / (2NC), d-chunk (q / 2) % NC, query tile q % 2,
+  // so the first key tile of the next block is formed while the first key
+  // tile of this block is consumed. Operand p = q / 2 (K tile p / NC,
+  // d-chunk p % NC) serves both query tiles.
+  // first step that uses score operand p
+  static constexpr int qk_first(int p) {
+    for (int s = 0; s < M; ++s)
+      if (pv_chunk(s) < 0 && qk_index(s) == 2 * p) return s;
+    return -1;
+  }
   static constexpr bool valid() {
     int qk = 0;
     for (int s = 0; s < M; ++s) qk += pv_chunk(s) < 0 ? 1 : 0;
     for (int g = 0; g + 1 < 4; ++g)
-      if (pv_start(g + 1) < pv_start(g) + ND) return false;
-    return qk == 2 * NC && pv_start(3) + ND == M;
+      if (pv_start(g + 1) < pv_start(g) + 2 * ND) return false;
+    return qk == 4 * NC && pv_start(3) + 2 * ND == M;
   }
 };
 static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
@@ -165,13 +235,14 @@ __device__ __forceinline__ void issue_tile(const u16* g, long stride, int k0, in
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdParams p, int n_qt) {
   using T = Tile<D>;
+  using PL = Plan<D>;
   constexpr int NC = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int ND = D / 32;  // 32-row tiles of O^T
-  // K runs one block ahead of V: block j's scores are formed while block
-  // j-1's probabilities meet V, so each tensor has its own two buffers.
+  // K runs one block ahead of V: block j+1's scores are formed while block
+  // j's probabilities meet V, so each tensor has its own two buffers.
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[T::kBytes];
@@ -236,38 +307,56 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   const u16* kg = static_cast<const u16*>(p.k) + k_tok0 * kstride + static_cast<long>(kvh) * D;
   const u16* vg = static_cast<const u16*>(p.v) + k_tok0 * kstride + static_cast<long>(kvh) * D;
 
+  // Blocks the workgroup streams, and blocks this wave computes: a causal
+  // wave stops at the block holding its own diagonal, and a wave whose rows
+  // all lie past the end of the queries computes nothing (it still loads
+  // its share of every tile and meets every barrier).
   int kend = Lk;
   if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
   const int nblk = (kend + kBC - 1) / kBC;
+  const int wq0 = q0 + 64 * w;  // first query row of this wave
+  int nblk_w = wq0 >= Lq ? 0 : nblk;
+  if (CAUSAL) nblk_w = min(nblk_w, wq0 / kBC + 1);
+
   if (nblk > 0) {
     issue_tile<D>(kg, kstride, 0, Lk, kb0, tid, w);
     issue_tile<D>(vg, kstride, 0, Lk, vb0, tid, w);
     if (nblk > 1) issue_tile<D>(kg, kstride, kBC, Lk, kb1, tid, w);
   }
 
-  const int wq0 = q0 + 32 * w;  // first query row of this wave
-  const int qrow = wq0 + j;     // this lane's query row
-
   // A negative scale is applied by negating Q (exact in bf16), so that the
   // base-2 factor c below is >= 0 and max(c*s) = c*max(s).
   const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // Q fragment, held in registers for the whole key loop: the B operand of
-  // S^T = K Q^T (column = query, 8 consecutive d values per lane).
-  bf16x8 qf[NC];
+  // Q fragments, held in registers for the whole key loop: the B operand of
+  // S^T = K Q^T (column = query, 8 consecutive d values per lane). Query
+  // tile qt of this wave covers rows wq0 + 32qt .. +31; this lane's row is
+  // wq0 + 32qt + j.
+  bf16x8 qf[2][NC];
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (qrow < Lq) v = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2) ^ qflip;
-    qf[cc] = as_bf16x8(v);
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = wq0 + 32 * qt + j;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow < Lq) v = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2) ^ qflip;
+      qf[qt][cc] = as_bf16x8(v);
+      asm volatile("" : "+a"(qf[qt][cc]));  // move to an AGPR now
+    }
   }
+  asm volatile("s_nop 4" ::: "memory");     // AGPR writes before MFMA reads
 
-  f32x16 acc[ND];
+  f32x16 acc[2][ND];
 #pragma unroll
-  for (int t = 0; t < ND; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;  // running reference of x = c * s
-  float l_run = 0.f;        // this lane's part of the running denominator
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      acc[qt][t] = f32x16{};
+      asm volatile("" : "+a"(acc[qt][t]));
+    }
+  float m_run[2] = {-INFINITY, -INFINITY};  // running reference of x = c * s
+  float l_run[2] = {0.f, 0.f};              // this lane's part of the denominator
 
   // Per-lane constants of the LDS reads.
   const int k_row_off = j * T::kRowBytes;            // + kt * 32 rows
@@ -281,16 +370,16 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     const int unit = (2 * cc + h2) ^ k_swz;
     return *reinterpret_cast<const bf16x8*>(ks + kt * 32 * T::kRowBytes + k_row_off + unit * 16);
   };
-  // V^T A operand for 32 d-rows (tile t) and 16 keys (chunk cc): two
-  // transposing reads give keys 16cc + 8r + 4*tr_h + (0..3), r = 0, 1, at
+  // V^T A operand for 32 d-rows (tile t) and 16 keys (chunk g): two
+  // transposing reads give keys 16g + 8r + 4*tr_h + (0..3), r = 0, 1, at
   // d column 32t + 16*tr_dgrp + tr_i. Lane tr_i of each 16-lane group
   // supplies the address of 4 consecutive d values of key row
-  // (16cc + 8r + 4*tr_h + tr_i/4).
-  auto v_operand = [&](const unsigned char* vs, int t, int cc) {
+  // (16g + 8r + 4*tr_h + tr_i/4).
+  auto v_operand = [&](const unsigned char* vs, int t, int g) {
     s16x4 half[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int row = 16 * cc + 8 * r + 4 * tr_h + (tr_i >> 2);
+      const int row = 16 * g + 8 * r + 4 * tr_h + (tr_i >> 2);
       const int unit = (4 * t + 2 * tr_dgrp + ((tr_i & 3) >> 1)) ^ swz<T::kUnits>(row);
       const int off = row * T::kRowBytes + unit * 16 + (tr_i & 1) * 8;
       half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + off));
@@ -299,147 +388,198 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
                               __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // S^T for two 32-key tiles of one block: s[kt][r] is the score of key
-  // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query qrow.
-  f32x16 sa[2], sb[2];
+  // S^T of one block: s[qt][kt][r] is the score of key
+  // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query wq0 + 32qt + j.
+  f32x16 sa[2][2], sb[2][2];
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (nblk > 0) {
+  if (nblk_w > 0) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sa[kt] = f32x16{};
+    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
-        sa[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kb0, kt, cc), qf[cc], sa[kt],
-                                                         0, 0, 0);
-    }
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 a = k_operand(kb0, kt, cc);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          if (cc == 0) sa[qt][kt] = mfma_qk_first(a, qf[qt][cc]);
+          else mfma_qk_acc(sa[qt][kt], a, qf[qt][cc]);
+        }
+      }
   }
 
   // One key block j: its scores sc are in registers. On entry the loads of
   // K_{j+1} and V_j are in flight (issued one block earlier).
-  //   1. wait for them, barrier (every wave is done with block j-1, so the
-  //      buffers of K_j and V_{j-1} are free), start the loads of K_{j+2}
-  //      and V_{j+1} into those buffers;
-  //   2. mask, row maximum, reference update (rare rescale);
-  //   3. the M steps of Plan<D>: the scores of block j+1 (sn) from K_{j+1},
-  //      the exponentials of block j, and O^T += V_j^T P_j^T, one MFMA per
-  //      step, so the matrix cores run while the vector unit computes
-  //      exponentials. Operands are read from LDS kAhead steps early.
-  using PL = Plan<D>;
+  //   head: wait for them, barrier (every wave is done with block j-1, so
+  //      the buffers of K_j and V_{j-1} are free), start the loads of
+  //      K_{j+2} and V_{j+1} into those buffers;
+  //   body: mask, row maxima, reference; then the M steps of Plan<D>: the
+  //      scores of block j+1 (sn) from K_{j+1}, the exponentials of block j,
+  //      and O^T += V_j^T P_j^T, one MFMA per step, so the matrix cores run
+  //      while the vector unit computes exponentials. Operands are read from
+  //      LDS kAhead steps early.
   constexpr int kAhead = 2;
-  auto iter = [&](auto par_tag, int jb, f32x16(&sc)[2], f32x16(&sn)[2]) {
+  auto head = [&](auto par_tag, int jb) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
-    unsigned char* k_next = PAR ? kb0 : kb1;        // K_{j+1}
     unsigned char* k_free = PAR ? kb1 : kb0;        // K_j, consumed
-    unsigned char* v_cur = PAR ? vb1 : vb0;         // V_j
     unsigned char* v_free = PAR ? vb0 : vb1;        // V_{j-1}, consumed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (jb + 2 < nblk) issue_tile<D>(kg, kstride, (jb + 2) * kBC, Lk, k_free, tid, w);
     if (jb + 1 < nblk) issue_tile<D>(vg, kstride, (jb + 1) * kBC, Lk, v_free, tid, w);
+  };
+  auto body = [&](auto par_tag, int jb, f32x16(&sc)[2][2], f32x16(&sn)[2][2]) {
+    constexpr int PAR = decltype(par_tag)::value;  // jb & 1
+    const unsigned char* k_next = PAR ? kb0 : kb1;  // K_{j+1}
+    const unsigned char* v_cur = PAR ? vb1 : vb0;   // V_j
+    if (jb >= nblk_w) return;
     const int k0 = jb * kBC;
+    mfma_result_guard();  // the last score MFMAs of sc may still be in flight
 
-    bf16x8 opnd[PL::M];
-    auto load_operand = [&](auto S) {
-      constexpr int g = PL::pv_chunk(S);
-      if constexpr (g < 0) {
-        constexpr int q = PL::qk_index(S);
-        opnd[S] = k_operand(k_next, q & 1, q >> 1);
-      } else {
-        opnd[S] = v_operand(v_cur, S - PL::pv_start(g), g);
-      }
+    // LDS operands: score operand p (K tile p/NC, d-chunk p%NC) is first used
+    // at step qk_first(p); value operand (t, g) at pv_start(g) + 2t.
+    bf16x8 kop[2 * NC];
+    bf16x8 vop[4][ND];
+    auto load_for_step = [&](auto S) {
+      static_for<2 * NC>([&](auto P) {
+        if constexpr (PL::qk_first(P) == S) kop[P] = k_operand(k_next, P / NC, P % NC);
+      });
+      static_for<4>([&](auto G) {
+        static_for<ND>([&](auto TT) {
+          if constexpr (PL::pv_start(G) + 2 * TT == S) vop[G][TT] = v_operand(v_cur, TT, G);
+        });
+      });
     };
-    static_for<kAhead>(load_operand);
 
     // Only blocks that reach past the end of the keys or cross the causal
-    // diagonal are masked: visible iff key <= lim, with key - k0 - 4*h2 =
-    // 32kt + 8(r/4) + (r%4). c >= FLT_MIN keeps 2^(c * -inf - m) = 0.
+    // diagonal of this wave are masked: visible iff key <= lim, with
+    // key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4). c >= FLT_MIN keeps
+    // 2^(c * -inf - m) = 0.
     if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0)) {
-      const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const int qrow = wq0 + 32 * qt + j;
+        const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sc[kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[kt][r] : -INFINITY;
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sc[qt][kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[qt][kt][r] : -INFINITY;
+      }
     }
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    float mb[2];
+    bool up = false;
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = fmaxf(sc[qt][0][0], sc[qt][0][1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    const float mb = xhalf_max(mx) * c;
-    // The reference point moves only when some row of the wave gains more
-    // than kLazy over it (wave-uniform decision).
-    const bool raise = __any(mb > m_run + kLazy);
-    if (raise) {
-      const float m_new = fmaxf(m_run, mb);
-      // A row that has seen no visible key keeps m = -inf; 0 is used as the
-      // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[qt][0][r]);
 #pragma unroll
-      for (int t = 0; t < ND; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qt][1][r]);
+      mb[qt] = xhalf_max(mx) * c;
+      // A row's first visible block sets its reference (its accumulator and
+      // denominator are still zero); later raises need the rescale.
+      if (m_run[qt] == -INFINITY) m_run[qt] = mb[qt];
+      up = up || (mb[qt] > m_run[qt] + kRaise);
     }
-    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+    if (__any(up)) {  // wave-uniform, rare
+      mfma_result_guard();  // the last P V MFMAs may still be in flight
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        // raise each row of this wave to its block maximum (alpha = 1 for
+        // rows that do not gain)
+        const float m_new = fmaxf(m_run[qt], mb[qt]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+        m_run[qt] = m_new;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) acc[qt][t] = scale_via_scratch(acc[qt][t], alpha);
+      }
+      asm volatile("s_nop 1" ::: "memory");  // AGPR writes before MFMA reads
+    }
+    static_for<kAhead>(load_for_step);
+    // A row that has seen no visible key keeps m = -inf; 0 is used as the
+    // reference then, so that 2^(-inf - ref) = 0 instead of NaN.
+    float m_ref[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) m_ref[qt] = (m_run[qt] == -INFINITY) ? 0.f : m_run[qt];
 
     // P^T as the B operand of O^T += V^T P^T: 16-key chunk g takes score
-    // registers 8(g%2) .. 8(g%2)+7 of tile g/2, i.e. keys
-    // 16g + 8(s/4) + 4*h2 + (s%4) for slot s.
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 pb[4];
+    // registers 8(g%2) .. 8(g%2)+7 of key tile g/2, i.e. keys
+    // 16g + 8(s/4) + 4*h2 + (s%4) for slot s. Element e of the block is
+    // chunk e/16, query tile (e/8)%2, slot e%8.
+    float rs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    bf16x8 pb[2][4];
     static_for<PL::M>([&](auto S) {
-      if constexpr (S + kAhead < PL::M) load_operand(std::integral_constant<int, S + kAhead>{});
+      if constexpr (S + kAhead < PL::M) load_for_step(std::integral_constant<int, S + kAhead>{});
       constexpr int g = PL::pv_chunk(S);
       if constexpr (g < 0) {
         constexpr int q = PL::qk_index(S);
-        constexpr int kt = q & 1, cc = q >> 1;
-        sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[S], qf[cc],
-                                                         cc == 0 ? f32x16{} : sn[kt], 0, 0, 0);
+        constexpr int qt = q & 1, pp = q >> 1, kt = pp / NC, cc = pp % NC;
+        if constexpr (cc == 0) sn[qt][kt] = mfma_qk_first(kop[pp], qf[qt][cc]);
+        else mfma_qk_acc(sn[qt][kt], kop[pp], qf[qt][cc]);
       } else {
-        constexpr int t = S - PL::pv_start(g);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[S], pb[g], acc[t], 0, 0, 0);
+        constexpr int i = S - PL::pv_start(g);
+        constexpr int t = i >> 1, qt = i & 1;
+        acc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g][t], pb[qt][g], acc[qt][t],
+                                                             0, 0, 0);
+        asm volatile("" : "+a"(acc[qt][t]));  // the accumulator lives in AGPRs
       }
-      static_for<32>([&](auto E) {
-        if constexpr (PL::elem_step(E) == S) {
-          constexpr int eg = E / 8, es = E % 8;
+      constexpr int e0 = PL::first_elem(S);
+      static_for<PL::first_elem(S + 1) - e0>([&](auto EI) {
+        constexpr int E = e0 + EI;
+        if constexpr (E < 64) {
+          constexpr int eg = E / 16, eq = (E / 8) & 1, es = E % 8;
           const float x = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[eg >> 1][8 * (eg & 1) + es], c, -m_ref));
-          rs[eg] += x;
-          pb[eg][es] = static_cast<__bf16>(x);
+              __builtin_fmaf(sc[eq][eg >> 1][8 * (eg & 1) + es], c, -m_ref[eq]));
+          rs[eq][eg] += x;
+          pb[eq][eg][es] = static_cast<__bf16>(x);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);  // from the unrounded float32 P
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)  // from the unrounded float32 P
+      l_run[qt] += (rs[qt][0] + rs[qt][1]) + (rs[qt][2] + rs[qt][3]);
   };
 
-  // The last block also forms the scores of a block past the end (from the
-  // stale K buffer, discarded): one branch-free loop body for every block.
+  // Key loop, unrolled by two so every LDS address has a fixed buffer. A
+  // wave's last computed block also forms the scores of the block after it
+  // (from whatever the K buffer holds, discarded): one branch-free region
+  // for every block.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   for (int jb = 0; jb < nblk; jb += 2) {
-    iter(std::integral_constant<int, 0>{}, jb, sa, sb);
+    head(P0{}, jb);
+    body(P0{}, jb, sa, sb);
     if (jb + 1 >= nblk) break;
-    iter(std::integral_constant<int, 1>{}, jb + 1, sb, sa);
+    head(P1{}, jb + 1);
+    body(P1{}, jb + 1, sb, sa);
   }
 
   // Epilogue: o = a / l, rounded once to bf16; LSE = ln(2) * (m + log2 l).
-  const float l_tot = xhalf_sum(l_run);
-  if (qrow < Lq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    u16* og = static_cast<u16*>(p.o) + (q_tok0 + qrow) * qstride + static_cast<long>(h) * D;
+  mfma_result_guard();  // the last P V MFMAs may still be in flight
 #pragma unroll
-    for (int t = 0; t < ND; ++t)
+  for (int qt = 0; qt < 2; ++qt) {
+    f32x16 o_t[ND];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 o4;
+    for (int t = 0; t < ND; ++t) o_t[t] = read_agpr(acc[qt][t]);
+    const int qrow = wq0 + 32 * qt + j;
+    const float l_tot = xhalf_sum(l_run[qt]);
+    if (qrow < Lq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      u16* og = static_cast<u16*>(p.o) + (q_tok0 + qrow) * qstride + static_cast<long>(h) * D;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = static_cast<__bf16>(acc[t][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(og + 32 * t + 8 * g + 4 * h2) = o4;
-      }
-    if (h2 == 0)
-      p.lse[lse_base + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int t = 0; t < ND; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = static_cast<__bf16>(o_t[t][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(og + 32 * t + 8 * g + 4 * h2) = o4;
+        }
+      if (h2 == 0)
+        p.lse[lse_base + qrow] = l_tot > 0.f ? (m_run[qt] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 

@@ -34,7 +34,7 @@ hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);
 
 // Query tile height of each kernel (rows of Q per workgroup); the host uses
 // it to bound the grid size.
-constexpr int kBf16TileRows = 128;
+constexpr int kBf16TileRows = 256;
 constexpr int kFp32TileRows = 64;
 
 }  // namespace fa
