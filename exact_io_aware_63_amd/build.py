@@ -2,6 +2,8 @@
 
 Run ``python exact_io_aware_63_amd/build.py`` (or ``__graft_entry__.build()``).
 It imports nothing from the package, so it runs before libfa.so exists.
+Each source is compiled to its own object in ``_build/`` (in parallel), then
+the objects are linked into the shared library.
 """
 from __future__ import annotations
 
@@ -12,7 +14,12 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_fp32.hip"]
+OBJ_DIR = os.path.join(os.path.dirname(PKG), "_build")
+# (source, object name, extra defines): the bf16 kernel source is compiled
+# once per (head width, causal) instance.
+SOURCES = [("fa_api.cpp", "fa_api", []), ("fa_fwd_fp32.hip", "fa_fwd_fp32", [])] + [
+    ("fa_fwd_bf16.hip", f"fa_fwd_bf16_d{d}_c{c}", [f"-DFA_BF16_D={d}", f"-DFA_BF16_CAUSAL={c}"])
+    for d in (128, 64) for c in (1, 0)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -20,28 +27,51 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU ops are kept off (v_pk_* fp32 forms are not used)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
 ]
 
 
+def _noise_free(text: str) -> str:
+    return "\n".join(ln for ln in text.splitlines()
+                     if ln.strip() and "packed-fp32-ops" not in ln
+                     and "not a recognized feature" not in ln)
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP/C++ source of the library into ``libfa.so``."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every HIP/C++ source of the library and link ``libfa.so``."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    procs = []
+    objs = []
+    for src, name, defines in SOURCES:
+        obj = os.path.join(OBJ_DIR, name + ".o")
+        cmd = [HIPCC, *FLAGS, *defines, *(extra_flags or []), "-c", "-o", obj,
+               os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+        objs.append(obj)
+    failed = []
+    for src, proc in procs:
+        out, _ = proc.communicate()
+        msg = _noise_free(out)
+        if proc.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(out)
+        elif verbose and msg:
+            print(msg)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", tmp, *srcs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    noise = [ln for ln in (res.stdout + res.stderr).splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
-    if verbose and noise:
-        print("\n".join(noise))
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -130,7 +130,13 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.causal = causal ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = bf16 ? fa::launch_fwd_bf16(p, s) : fa::launch_fwd_fp32(p, s);
+  hipError_t e;
+  if (!bf16)
+    e = fa::launch_fwd_fp32(p, s);
+  else if (d == 64)
+    e = causal ? fa::launch_fwd_bf16<64, true>(p, s) : fa::launch_fwd_bf16<64, false>(p, s);
+  else
+    e = causal ? fa::launch_fwd_bf16<128, true>(p, s) : fa::launch_fwd_bf16<128, false>(p, s);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

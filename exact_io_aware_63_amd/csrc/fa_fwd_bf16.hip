@@ -583,19 +583,23 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   }
 }
 
+}  // namespace
+
+// One object file per (head width, causal) pair: the build compiles this
+// source once for each, with FA_BF16_D in {64, 128} and FA_BF16_CAUSAL in
+// {0, 1}, so the four kernels compile in parallel.
 template <int D, bool CAUSAL>
-hipError_t launch(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int n_qt = (p.nq + kBR - 1) / kBR;
   const unsigned grid = static_cast<unsigned>(n_qt) * p.hq * p.batch;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p, n_qt);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-}
+#if !defined(FA_BF16_D) || !defined(FA_BF16_CAUSAL)
+#error "compile with -DFA_BF16_D=64|128 -DFA_BF16_CAUSAL=0|1"
+#endif
+template hipError_t launch_fwd_bf16<FA_BF16_D, (FA_BF16_CAUSAL != 0)>(const FwdParams&,
+                                                                    hipStream_t);
 
 }  // namespace fa

@@ -25,9 +25,15 @@ struct FwdParams {
   int causal;
 };
 
-// Launch the bf16 kernel (d in {64, 128}). Returns the hipError_t of the
-// launch.
+// Launch the bf16 kernel for head width D (64 or 128), causal or not.
+// Returns the hipError_t of the launch. Each of the four instances is
+// compiled in its own object file.
+template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+extern template hipError_t launch_fwd_bf16<64, false>(const FwdParams&, hipStream_t);
+extern template hipError_t launch_fwd_bf16<64, true>(const FwdParams&, hipStream_t);
+extern template hipError_t launch_fwd_bf16<128, false>(const FwdParams&, hipStream_t);
+extern template hipError_t launch_fwd_bf16<128, true>(const FwdParams&, hipStream_t);
 
 // Launch the float32 kernel (d in {64, 128}).
 hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);

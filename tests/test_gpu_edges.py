@@ -263,3 +263,41 @@ def test_peaky_rows_parity():
     o, lse = run_gpu(inp, True, 1 / math.sqrt(128))
     o_ref, lse_ref = oracle.attention_ref(inp.q, inp.k, inp.v, 1 / math.sqrt(128), True)
     assert_parity(o, lse, o_ref, lse_ref, "bf16", "peaky rows")
+
+
+def _ramp_inputs(n, d, hq, hkv, seed, per_tile):
+    """Seeded bf16 inputs plus a key-position ramp in the last d column: q
+    holds A there for every row and key j holds floor(j / 32), so each run of
+    32 keys scores per_tile more (base-2 units) than the run before it."""
+    inp = W.draw(1, hq, hkv, n, n, d, "bf16", seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    a = float(W.bf16_bits_to_f32(W.round_to_bf16_bits(
+        np.float32([per_tile / (scale * 1.4426950408889634)])))[0])
+    ramp = np.floor(np.arange(n) / 32.0).astype(np.float32)
+    inp.q[..., -1] = a
+    inp.q_bits[..., -1] = W.round_to_bf16_bits(np.float32([a]))[0]
+    inp.k[0, :, :, -1] = ramp[:, None]
+    inp.k_bits[0, :, :, -1] = W.round_to_bf16_bits(ramp)[:, None]
+    return inp, scale
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_raising_reference_every_tile(d, causal):
+    """Scores that climb by about 20 (base 2) every 32 keys: each later tile
+    exceeds the row's reference by more than 2^16, so the reference is raised
+    and the accumulators rescaled many times per row."""
+    say(f"[case] rising scores d={d} causal={causal}")
+    inp, scale = _ramp_inputs(700, d, 4, 2, 41, 20.0)
+    o, lse = run_gpu(inp, causal, scale)
+    o_ref, lse_ref = oracle.attention_ref(inp.q, inp.k, inp.v, scale, causal)
+    assert_parity(o, lse, o_ref, lse_ref, "bf16", "rising scores")
+
+
+def test_falling_scores_underflow_later_tiles():
+    """Scores that drop by about 20 (base 2) every 32 keys: the first tile
+    sets the reference and later weights underflow, as in the definition."""
+    say("[case] falling scores")
+    inp, scale = _ramp_inputs(700, 128, 4, 2, 42, -20.0)
+    o, lse = run_gpu(inp, True, scale)
+    o_ref, lse_ref = oracle.attention_ref(inp.q, inp.k, inp.v, scale, True)
+    assert_parity(o, lse, o_ref, lse_ref, "bf16", "falling scores")
