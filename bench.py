@@ -12,17 +12,25 @@ Prints one JSON line with the throughput in TFLOP/s (algorithmic flops:
 MFMA bound) and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host.
 
-    python bench.py [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 4] [--seq-len N]
+                    [--no-cpu-baseline]
+
+``--seq-len`` replaces N of a fixed-length workload (same heads, d, mask
+and input recipe), e.g. to measure HBM traffic against N.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
 import os
 import re
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -153,6 +161,38 @@ def cpu_baseline(inp, w, budget_s: float = 12.0):
 
 
 # ---------------------------------------------------------------------------
+# Shader clock under load
+# ---------------------------------------------------------------------------
+
+def sclk_under_load(step, sync, launch_ms: float, seconds: float = 1.5):
+    """Mean GFX clock (MHz) over the XCDs, read with ``amd-smi metric --clock``
+    while about ``seconds`` of back-to-back launches run; None without amd-smi."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    out = {}
+
+    def sample():
+        time.sleep(min(0.4, seconds / 3))
+        try:
+            out["text"] = subprocess.run([exe, "metric", "-g", "0", "--clock"], capture_output=True,
+                                         text=True, timeout=30).stdout
+        except Exception:  # pragma: no cover - tool failure leaves the figure empty
+            out["text"] = ""
+
+    n = max(1, int(seconds / max(launch_ms * 1e-3, 1e-6)))
+    th = threading.Thread(target=sample)
+    th.start()
+    for _ in range(n):
+        step()
+    sync()
+    th.join()
+    clocks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out.get("text", ""))]
+    return {"mean": float(np.mean(clocks)), "min": min(clocks), "max": max(clocks),
+            "xcds": len(clocks)} if clocks else None
+
+
+# ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
 
@@ -163,6 +203,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed launches first (also brings the GPU clock up)")
     ap.add_argument("--workload", type=int, default=4, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--seq-len", type=int, default=0, metavar="N",
+                    help="override N of a fixed-length workload")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip reading the shader clock under load (amd-smi)")
+    ap.add_argument("--cold-launches", type=int, default=5,
+                    help="launches timed after writing a 512 MiB scrub buffer (cold L2/MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -196,8 +242,19 @@ def main(argv=None):
     import exact_io_aware_63_amd as fa
 
     w = W.WORKLOADS[args.workload]
+    headline = args.workload == 4
     t_gen = time.perf_counter()
-    inp = W.draw_workload(args.workload)
+    if args.seq_len:
+        if w.packed:
+            print("--seq-len applies to fixed-length workloads only", file=sys.stderr)
+            return 2
+        headline = headline and args.seq_len == w.n
+        w = dataclasses.replace(w, n=args.seq_len,
+                                name=re.sub(r"N=\d+", f"N={args.seq_len}", w.name))
+        inp = W.draw(w.batch, w.hq, w.hkv, w.n, w.n, w.d, w.dtype, 1000 + w.wid,
+                     (w.sigma_q, w.sigma_k, w.sigma_v))
+    else:
+        inp = W.draw_workload(args.workload)
     lens_q, lens_k = workload_lens(inp, w)
     if w.dtype == "bf16":
         def up(bits):
@@ -247,6 +304,26 @@ def main(argv=None):
     per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
     total_ms = events[0].elapsed_time(events[-1])
 
+    # Cold launches: a 512 MiB write between launches evicts Q, K, V from the
+    # L2 caches and the 256 MB last-level cache; each launch is bracketed by
+    # its own events.
+    cold_ms = []
+    if args.cold_launches > 0:
+        scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        for i in range(args.cold_launches):
+            scrub.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del scrub
+
+    sclk = None
+    if not args.no_sclk:
+        sclk = sclk_under_load(step, torch.cuda.synchronize, float(np.mean(per_launch_ms)))
+
     ok = bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
 
     flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal)
@@ -259,13 +336,13 @@ def main(argv=None):
     if w.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": recorded_traffic() if args.workload == 4 else None}
+                "traffic": recorded_traffic() if headline else None}
     else:
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None}
 
     line = {
-        "metric": METRIC if args.workload == 4 else f"attention fwd TFLOP/s ({w.name})",
+        "metric": METRIC if headline else f"attention fwd TFLOP/s ({w.name})",
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -283,6 +360,11 @@ def main(argv=None):
                    "causal": w.causal, "parallelism": "single GPU"},
         "roofline": roof,
         "pct_of_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS if w.dtype == "bf16" else None,
+        # the same against the peak at the clock amd-smi reads under this load
+        # (4096 flop/clk/CU x 256 CUs x measured GFX clock)
+        "pct_of_mfma_peak_at_measured_sclk": (
+            100.0 * value / (PEAK_BF16_TFLOPS * sclk["mean"] / 2400.0)
+            if (w.dtype == "bf16" and sclk) else None),
         "detail": {
             "alg_flops": flops,
             "alg_hbm_bytes": abytes,
@@ -290,10 +372,13 @@ def main(argv=None):
             "launch_ms": {"mean": avg_launch_ms, "min": float(np.min(per_launch_ms)),
                           "median": float(np.median(per_launch_ms)),
                           "max": float(np.max(per_launch_ms))},
+            "cold_launch_ms": ({"median": float(np.median(cold_ms)), "min": float(np.min(cold_ms)),
+                                "launches": len(cold_ms)} if cold_ms else None),
             "host_wall_s": wall,
             "input_gen_s": gen_s,
             "outputs_finite": ok,
             "kernel_source_sha256_16": kernel_source_hash(),
+            "sclk_mhz_under_load": sclk,
             "device": torch.cuda.get_device_name(dev),
         },
     }

@@ -1,8 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Small shapes are compared element by element over the whole output; they
-span several 128-row query tiles, ragged tails, Nq != Nk, GQA/MQA and packed
-sequences of lengths 0, 1, 127, 128, 129. The five named workloads run at
+span several query tiles (256 rows in bf16, 64 in fp32), ragged tails,
+Nq != Nk, GQA/MQA and packed sequences of lengths 0, 1, 127, 128, 129. The
+larger causal cases (hundreds of query tiles, odd tile counts, packed
+sequences of mixed lengths) cover both workgroup orders: K/V heads a
+multiple of 8 (each K/V head kept on one XCD) or not. The five named workloads run at
 their full sizes in the launch configuration the bench times; the largest
 ones are compared on sampled rows (every sequence's boundary rows plus
 random ones) that the oracle forms one by one.
@@ -41,6 +44,11 @@ SMALL = [
     ("bf16", 1, 4, 2, 0, 0, 128, True, [1, 127, 128, 129, 300, 0, 64, 513]),
     ("bf16", 1, 4, 2, 0, 0, 128, False, [1, 127, 128, 129, 300, 0, 64, 513]),
     ("bf16", 1, 8, 2, 0, 0, 64, True, [5, 260, 0, 128, 77]),
+    # many causal query tiles, both workgroup orders
+    ("bf16", 2, 96, 8, 600, 600, 128, True, None),
+    ("bf16", 3, 66, 3, 700, 700, 64, True, None),
+    ("bf16", 1, 32, 8, 0, 0, 128, True, [1000, 37, 513, 256, 700, 1, 0, 300]),
+    ("bf16", 1, 32, 8, 0, 0, 64, True, [900, 5, 512, 257, 0, 640, 129, 1]),
     ("fp32", 2, 4, 2, 300, 300, 128, True, None),
     ("fp32", 1, 4, 1, 200, 333, 64, False, None),
     ("fp32", 1, 2, 1, 333, 200, 128, True, None),
