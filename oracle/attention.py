@@ -28,6 +28,17 @@ Readings taken where the pages are silent:
 * a row that sees no key has O = 0 and LSE = -inf;
 * no additive bias B, and V has the same width d as Q and K.
 
+The backward pass (``attention_head_bwd`` and the functions after it) is
+the gradient of the same function with respect to Q, K and V for a given
+upstream gradient dO, written out by the chain rule through the
+materialised S and P. The pages name this step only: "Understanding
+FlashAttention Pt 1", contents, section 3.6 ("Backward pass: recompute
+instead of save"), and semiaifoundry "attention-io-tiling", section
+*Specifications and interfaces* (use the retained statistics and permitted
+recomputation for the backward execution). The oracle recomputes nothing
+from retained statistics: it forms S and P from Q and K again, exactly as
+the forward definition reads, and differentiates that.
+
 Everything is float64. bf16 and fp32 inputs are exactly representable in
 float64, so the upcast adds no error.
 
@@ -209,3 +220,151 @@ def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None
         lse[sel] = l_sel
         i0 = i1
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: gradients of O = softmax(scale Q K^T) V
+# ---------------------------------------------------------------------------
+
+def softmax_rows_bwd(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """Chain rule through the row softmax: given P = softmax_row(S) and
+    dP = dL/dP, returns dS = dL/dS with dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik).
+
+    Derivation: dP_ik/dS_ij = P_ik (delta_kj - P_ij) for a row softmax
+    ("Softmax does not need the matrix", *Carry the Normalizer*, stable
+    softmax p_j = exp(s_j - m) / sum exp(s_i - m); the shift m cancels).
+    Masked entries have P = 0, hence dS = 0.
+    """
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def attention_head_bwd(q, k, v, do, scale: float, causal: bool):
+    """Gradients of one (sequence, head): q, do [Lq, d]; k, v [Lk, d].
+
+    Forms S = scale q K^T, the mask, P = softmax_row(S) (as the forward
+    definition), then
+      dV = P^T dO,   dP = dO V^T,   dS = softmax_rows_bwd(P, dP),
+      dQ = scale dS K,   dK = scale dS^T Q.
+    Returns (dq [Lq, d], dk [Lk, d], dv [Lk, d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    lq, lk = q.shape[0], k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if lq == 0 or lk == 0:
+        return dq, dk, dv
+    for c0 in range(0, lq, ROW_CHUNK):
+        r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
+        s = scores(q[r], k, scale)
+        s = np.where(visible_mask(r, lk, causal), s, -np.inf)
+        p, _, _ = softmax_rows(s)
+        dv += p.T @ do[r]
+        dp = do[r] @ v.T
+        ds = softmax_rows_bwd(p, dp)
+        dq[r] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r])
+    return dq, dk, dv
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None):
+    """Gradients in the layouts of the module docstring (dO like O).
+
+    Returns (dQ like q, dK like k, dV like v) as float64 arrays. With
+    grouped-query attention a K/V head's gradients are the sums over the
+    query heads that read it.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if cu_seqlens is None:
+        bsz, _, hq, _ = q.shape
+        hkv = k.shape[2]
+        for b in range(bsz):
+            for h in range(hq):
+                g = kv_head_of(h, hq, hkv)
+                a, bk, bv = attention_head_bwd(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h],
+                                               scale, causal)
+                dq[b, :, h] = a
+                dk[b, :, g] += bk
+                dv[b, :, g] += bv
+        return dq, dk, dv
+    hq, hkv = q.shape[1], k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            a, bk, bv = attention_head_bwd(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], do[lo:hi, h],
+                                           scale, causal)
+            dq[lo:hi, h] = a
+            dk[lo:hi, g] += bk
+            dv[lo:hi, g] += bv
+    return dq, dk, dv
+
+
+def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_picks,
+                         cu_seqlens=None):
+    """Selected gradient rows, for parity checks at sizes where the full
+    oracle would take too long.
+
+    ``q_picks`` [P, 3] of (s, h, i): the dQ row of query i of q-head h.
+    ``kv_picks`` [R, 3] of (s, g, j): the dK and dV rows of key j of K/V head
+    g, summed over the query heads that read g. Every row is formed from the
+    definition as in ``attention_head_bwd``: the whole rows of S, P and dP of
+    the queries involved are materialised. Returns (dq [P, d], dk [R, d],
+    dv [R, d]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    q_picks = np.asarray(q_picks, dtype=np.int64).reshape(-1, 3)
+    kv_picks = np.asarray(kv_picks, dtype=np.int64).reshape(-1, 3)
+    d = q.shape[-1]
+    if cu_seqlens is None:
+        hq, hkv = q.shape[2], k.shape[2]
+    else:
+        hq, hkv = q.shape[1], k.shape[1]
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+
+    def head(s, h):
+        g = kv_head_of(int(h), hq, hkv)
+        if cu_seqlens is None:
+            return (np.asarray(q[s, :, h], np.float64), np.asarray(k[s, :, g], np.float64),
+                    np.asarray(v[s, :, g], np.float64), np.asarray(do[s, :, h], np.float64))
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        return (np.asarray(q[lo:hi, h], np.float64), np.asarray(k[lo:hi, g], np.float64),
+                np.asarray(v[lo:hi, g], np.float64), np.asarray(do[lo:hi, h], np.float64))
+
+    dq = np.zeros((len(q_picks), d))
+    for n, (s, h, i) in enumerate(q_picks):
+        qh, kh, vh, doh = head(s, h)
+        r = np.array([i])
+        sc = np.where(visible_mask(r, kh.shape[0], causal), scores(qh[r], kh, scale), -np.inf)
+        p, _, _ = softmax_rows(sc)
+        ds = softmax_rows_bwd(p, doh[r] @ vh.T)
+        dq[n] = scale * (ds @ kh)[0]
+    dk = np.zeros((len(kv_picks), d))
+    dv = np.zeros((len(kv_picks), d))
+    group = hq // hkv
+    for n, (s, g, j) in enumerate(kv_picks):
+        for h in range(g * group, (g + 1) * group):
+            qh, kh, vh, doh = head(s, h)
+            lq, lk = qh.shape[0], kh.shape[0]
+            for c0 in range(0, lq, ROW_CHUNK):
+                r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
+                sc = np.where(visible_mask(r, lk, causal), scores(qh[r], kh, scale), -np.inf)
+                p, _, _ = softmax_rows(sc)
+                ds = softmax_rows_bwd(p, doh[r] @ vh.T)
+                dv[n] += p[:, j] @ doh[r]
+                dk[n] += scale * (ds[:, j] @ qh[r])
+    return dq, dk, dv
+
