@@ -4,11 +4,12 @@ Argument marshalling only: every step of the attention forward runs in the
 HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
-The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_status_string``,
+The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_bwd``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
 wrapper that checks torch tensors, allocates O and LSE with torch and calls
-``fa_fwd`` or ``fa_fwd_fp32`` on the current stream.
+``fa_fwd`` or ``fa_fwd_fp32`` on the current stream; ``attention_bwd`` does
+the same for ``fa_bwd`` (dQ, dK, dV and the Dsum scratch).
 
 Importing this package loads ``libfa.so`` from this directory and raises
 ImportError if it is missing: there is no fallback implementation.
@@ -44,6 +45,9 @@ _lib.fa_fwd.argtypes = _FWD_ARGS
 _lib.fa_fwd.restype = ctypes.c_int
 _lib.fa_fwd_fp32.argtypes = _FWD_ARGS
 _lib.fa_fwd_fp32.restype = ctypes.c_int
+_lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
+                        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
+_lib.fa_bwd.restype = ctypes.c_int
 _lib.fa_status_string.argtypes = [ctypes.c_int]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
@@ -51,7 +55,8 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_status_string", "fa_last_error", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_status_string", "fa_last_error",
+            "fa_version")
 
 
 class FaError(RuntimeError):
@@ -71,6 +76,13 @@ def fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlen
     """C ``fa_fwd_fp32``: pointers are integer device addresses (or 0 / None)."""
     return _lib.fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
                             cu_seqlens, stream)
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+           cu_seqlens, stream) -> int:
+    """C ``fa_bwd``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale,
+                       int(causal), cu_seqlens, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -148,3 +160,52 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return out, lse
+
+
+def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_seqlens=None,
+                  max_seqlen=None, stream=None):
+    """Gradients (dQ, dK, dV) of attention through the C ABI (bf16 only).
+
+    Tensors as ``attention_fwd`` takes and returns them (``o`` and ``lse``
+    from the forward call on the same inputs), ``do`` shaped like ``o``.
+    Allocates dQ, dK, dV and the float32 Dsum scratch with torch.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor")
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have q's shape")
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+            raise ValueError("fixed length wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
+        B, Nq, Hq, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+        cu_ptr = None
+    else:
+        if max_seqlen is None:
+            raise ValueError("packed input needs max_seqlen (host int)")
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        B = cu_seqlens.numel() - 1
+        Nq = Nk = int(max_seqlen)
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsum = torch.empty_like(lse)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsum.data_ptr(),
+                     B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cu_ptr, stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return dq, dk, dv

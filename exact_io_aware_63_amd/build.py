@@ -15,11 +15,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 OBJ_DIR = os.path.join(os.path.dirname(PKG), "_build")
-# (source, object name, extra defines): the bf16 kernel source is compiled
+# (source, object name, extra defines): each bf16 kernel source is compiled
 # once per (head width, causal) instance.
 SOURCES = [("fa_api.cpp", "fa_api", []), ("fa_fwd_fp32.hip", "fa_fwd_fp32", [])] + [
-    ("fa_fwd_bf16.hip", f"fa_fwd_bf16_d{d}_c{c}", [f"-DFA_BF16_D={d}", f"-DFA_BF16_CAUSAL={c}"])
-    for d in (128, 64) for c in (1, 0)]
+    (f"fa_{pas}_bf16.hip", f"fa_{pas}_bf16_d{d}_c{c}", [f"-DFA_BF16_D={d}", f"-DFA_BF16_CAUSAL={c}"])
+    for pas in ("fwd", "bwd") for d in (128, 64) for c in (1, 0)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

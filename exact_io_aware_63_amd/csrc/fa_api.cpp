@@ -4,6 +4,7 @@
 // error paths work (and are tested) on machines without a GPU.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -141,6 +142,90 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   return FA_OK;
 }
 
+// Checks of fa_bwd. Unlike the forward, an empty side does not make the
+// call a no-op: with Nq == 0 every dK and dV row is zero, and with Nk == 0
+// every dQ row is zero, and the kernels write those zeros.
+int validate_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* LSE, const void* dQ, const void* dK, const void* dV,
+                 const float* Dsum, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                 const int32_t* cu_seqlens, bool* noop) {
+  *noop = false;
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B=%d, Nq=%d, Nk=%d must be >= 0", B, Nq, Nk);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_SHAPE, "Hq=%d and Hkv=%d must be > 0", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (cu_seqlens != nullptr && Nq != Nk)
+    return fail(FA_ERR_SHAPE, "packed sequences need Nq == Nk (the maximum length); got %d, %d",
+                Nq, Nk);
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head width d=%d; supported: 64, 128", d);
+  if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
+  if (B == 0 || (Nq == 0 && Nk == 0)) {
+    *noop = true;
+    return FA_OK;
+  }
+  const bool has_q = Nq > 0, has_k = Nk > 0;
+  if ((has_q && (!Q || !O || !dO || !LSE || !Dsum || !dQ)) || (has_k && (!K || !V || !dK || !dV)))
+    return fail(FA_ERR_NULL,
+                "every buffer of a non-empty side must be non-NULL (query side: Q, O, dO, LSE, "
+                "Dsum, dQ; key side: K, V, dK, dV)");
+  const void* p16[] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* ptr : p16)
+    if (ptr && !aligned(ptr, 16))
+      return fail(FA_ERR_ARG, "Q, K, V, O, dO, dQ, dK and dV must be 16-byte aligned");
+  if ((LSE && !aligned(LSE, 16)) || (Dsum && !aligned(Dsum, 16)))
+    return fail(FA_ERR_ARG, "LSE and Dsum must be 16-byte aligned");
+  if (cu_seqlens && !aligned(cu_seqlens, 4))
+    return fail(FA_ERR_ARG, "cu_seqlens must be 4-byte aligned");
+  const long tiles = (static_cast<long>(std::max(Nq, Nk)) + 127) / 128;
+  if (tiles * std::max(Hq, Hkv) * static_cast<long>(B) > 0x7fffffffL ||
+      static_cast<long>(B) * Nq * Hq * (d / 8) > 0x7fffffffL * 256L)
+    return fail(FA_ERR_SHAPE, "problem exceeds the launch limits");
+  return FA_OK;
+}
+
+int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+            const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq, int Hkv,
+            int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
+            void* stream) {
+  g_last_error[0] = '\0';
+  bool noop = false;
+  int st = validate_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale,
+                        cu_seqlens, &noop);
+  if (st != FA_OK || noop) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::BwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = LSE;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.dsum = Dsum;
+  p.cu_seqlens = cu_seqlens;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.d = d;
+  p.scale = scale;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.causal = causal ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d == 64)
+    e = causal ? fa::launch_bwd_bf16<64, true>(p, s) : fa::launch_bwd_bf16<64, false>(p, s);
+  else
+    e = causal ? fa::launch_bwd_bf16<128, true>(p, s) : fa::launch_bwd_bf16<128, false>(p, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +240,14 @@ int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O, float*
                 int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                 const int32_t* cu_seqlens, void* stream) {
   return run(false, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq, int Hkv,
+           int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
+           void* stream) {
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 cu_seqlens, stream);
 }
 
 const char* fa_status_string(int status) {

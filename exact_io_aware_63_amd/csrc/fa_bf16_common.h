@@ -1,0 +1,95 @@
+// Pieces shared by the bf16 kernels of libfa (forward and backward): vector
+// types, the 64-row tile of K, V, Q or dO as staged in LDS (16-byte units of
+// each row XOR-swizzled), its buffer-to-LDS loader, lane reductions and a
+// compile-time loop. Device code only; every definition has internal
+// linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int kTileRows = 64;  // rows of one staged tile
+constexpr int kThreads = 256;  // threads per workgroup of the bf16 kernels
+// Third descriptor word of a raw buffer resource on gfx9-family parts
+// (32-bit data format, no swizzle); the range check uses num_records.
+constexpr int kBufferFlags = 0x00020000;
+
+template <int D>
+struct Tile {
+  static constexpr int kUnits = D / 8;                          // 16-byte units per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kTileRows * kRowBytes;          // one tile
+  static constexpr int kLoads = kTileRows * kUnits / kThreads;  // loads per lane per tile
+};
+
+// XOR swizzle of the 16-byte unit index within a row.
+template <int UNITS>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (UNITS == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+__device__ __forceinline__ u32x4 ld16(const u16* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// max and sum of a value with the same lane of the other half-wave
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Start the loads of one 64-row tile of a bf16 tensor with rows of D values
+// at element stride `stride` (rows r0 .. r0+63: keys of K or V, or queries
+// of Q or dO) into LDS. Each lane moves kLoads 16-byte units; a wave
+// instruction fills 1 KiB of contiguous LDS. Rows at or past L (the length
+// of the sequence) are outside the buffer range and are written as zeros.
+template <int D>
+__device__ __forceinline__ void issue_tile(const u16* g, long stride, int r0, int L,
+                                           unsigned char* dst, int tid, int w) {
+  using T = Tile<D>;
+  const int rows = min(L - r0, kTileRows);
+  const uint32_t stride_b = static_cast<uint32_t>(stride * 2);
+  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g + static_cast<long>(r0) * stride), 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int it = 0; it < T::kLoads; ++it) {
+    const int u = it * kThreads + tid;
+    const int row = u / T::kUnits;
+    const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
+    const uint32_t voff = row * stride_b + gc * 16;
+    const int lds_off = (it * kThreads + w * 64) * 16;  // wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + lds_off), 16, voff, 0, 0, 0);
+  }
+}
+
+}  // namespace
+}  // namespace fa

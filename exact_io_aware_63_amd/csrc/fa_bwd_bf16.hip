@@ -1,0 +1,502 @@
+// Exact attention backward by recomputation, bf16 in / bf16 out, float32
+// accumulation, for gfx950 (CDNA4) matrix cores.
+//
+// The forward pass keeps only O and the per-row log-sum-exp; the backward
+// pass recomputes the probabilities block by block from Q, K and that LSE
+// instead of reading a stored P ("Understanding FlashAttention Pt 1:
+// Personal Notes", contents, section 3.6: recompute instead of save;
+// semiaifoundry "attention-io-tiling", section Specifications and
+// interfaces: the retained statistics and permitted recomputation serve
+// the backward execution). With S = scale Q K^T and P = exp(S - LSE) on the
+// visible pairs, the gradients of O = P V for an upstream gradient dO are
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = dO_i . O_i,
+//   dQ = scale dS K,   dK = scale dS^T Q
+// (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j).
+//
+// Three kernels, launched in order on one stream:
+//   * bwd_dot_kernel: D = rowsum(dO * O) in float32, one value per (query
+//     row, q-head), laid out like the LSE;
+//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch or sequence,
+//     K/V head); wave w holds keys 32w .. 32w+31 of K and V in registers and
+//     accumulates dK^T and dV^T in registers while 64-row blocks of Q and dO
+//     (and their LSE and D) stream through LDS, for every query head of the
+//     K/V head's group, so grouped-query gradients are summed without
+//     atomics. Per 32 x 32 block: S = Q K^T and dP = dO V^T (lane = key,
+//     registers = queries), then P and dS, packed to bf16 as the B operands
+//     of dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from the
+//     row-major LDS tiles through ds_read_b64_tr_b16;
+//   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch or
+//     sequence, q-head); wave w holds rows 32w .. 32w+31 of Q and dO in
+//     registers (lane = query, one LSE and one D value per lane) and
+//     accumulates dQ^T while 64-key blocks of K and V stream through LDS:
+//     S^T = K Q^T and dP^T = V dO^T, then P^T and dS^T, and
+//     dQ^T += K^T dS^T with K^T read through transposing LDS reads.
+// The causal mask is top-left (key j visible to query i iff j <= i, indices
+// local to the batch entry or sequence); blocks entirely above the diagonal
+// are skipped per wave, and partial blocks are masked element by element.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "fa_bf16_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdRows = 128;  // keys (dK/dV kernel) or query rows (dQ kernel) per workgroup
+
+// Output register r of a 32x32 MFMA block sits at row 8(r/4) + 4*h2 + (r%4)
+// and column lane % 32, h2 = lane / 32.
+__device__ __forceinline__ constexpr int mrow(int r, int h2) { return 8 * (r >> 2) + 4 * h2 + (r & 3); }
+
+// Transposed A operand (32 rows of the tile's d columns, 16 of its rows) of
+// a 64-row LDS tile, e.g. dO^T, Q^T or K^T: two transposing reads give tile
+// rows 16g + 8r + 4*tr_h + (0..3), r = 0, 1, at d column 32t + 16*tr_dgrp +
+// tr_i; lane tr_i of each 16-lane group supplies the address of 4
+// consecutive d values of tile row 16g + 8r + 4*tr_h + tr_i/4. The row order
+// matches the MFMA output registers 8g .. 8g+7 (mrow) of a score block,
+// which become the B operand.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int row0, int t, int g,
+                                             int lane) {
+  using T = Tile<D>;
+  const int tr_i = lane & 15;
+  const int tr_dgrp = (lane >> 4) & 1;
+  const int tr_h = lane >> 5;
+  s16x4 half[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = row0 + 16 * g + 8 * r + 4 * tr_h + (tr_i >> 2);
+    const int unit = (4 * t + 2 * tr_dgrp + ((tr_i & 3) >> 1)) ^ swz<T::kUnits>(row);
+    const int off = row * T::kRowBytes + unit * 16 + (tr_i & 1) * 8;
+    half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + off));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row-major A operand (32 tile rows from row0, 16 d values of chunk cc) of a
+// 64-row LDS tile: lane reads row row0 + lane%32, d = 16cc + 8*h2 .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const unsigned char* tile, int row0, int cc, int lane) {
+  using T = Tile<D>;
+  const int row = row0 + (lane & 31);
+  const int unit = (2 * cc + (lane >> 5)) ^ swz<T::kUnits>(row);
+  return *reinterpret_cast<const bf16x8*>(tile + row * T::kRowBytes + unit * 16);
+}
+
+// B operand pair of registers 8g .. 8g+7 of a float32 MFMA output block,
+// rounded to bf16 (nearest even).
+__device__ __forceinline__ bf16x8 pack_chunk(const f32x16& x, int g) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(x[8 * g + i]);
+  return r;
+}
+
+// Index of the LSE / D value of token `tok` (sequence-local row i) of q-head
+// h: fixed length [B, Hq, Nq], packed [Hq, T].
+struct RowIndex {
+  long base;  // index of row 0 of this (batch or sequence, head)
+  __device__ __forceinline__ long at(int i) const { return base + i; }
+};
+
+// Sequence bounds of batch entry or sequence b.
+struct SeqBounds {
+  long q_tok0, k_tok0;  // first token of the sequence in Q/O/dO and in K/V
+  int Lq, Lk;
+  long total;           // packed: total tokens (LSE row stride), else Nq
+};
+__device__ __forceinline__ SeqBounds seq_bounds(const BwdParams& p, int b) {
+  SeqBounds s;
+  if (p.cu_seqlens != nullptr) {
+    const int s0 = p.cu_seqlens[b];
+    const int s1 = p.cu_seqlens[b + 1];
+    s.Lq = s.Lk = s1 - s0;
+    s.q_tok0 = s.k_tok0 = s0;
+    s.total = p.cu_seqlens[p.batch];
+  } else {
+    s.Lq = p.nq;
+    s.Lk = p.nk;
+    s.q_tok0 = static_cast<long>(b) * p.nq;
+    s.k_tok0 = static_cast<long>(b) * p.nk;
+    s.total = p.nq;
+  }
+  return s;
+}
+__device__ __forceinline__ RowIndex row_index(const BwdParams& p, const SeqBounds& s, int b, int h) {
+  RowIndex r;
+  r.base = p.cu_seqlens != nullptr ? static_cast<long>(h) * s.total + s.q_tok0
+                                   : (static_cast<long>(b) * p.hq + h) * p.nq;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+
+// One (token, q-head) row per D/8 lanes: each lane multiplies 8 bf16 pairs,
+// the row's lanes then add their partial sums. Rows are enumerated token by
+// token (tok * Hq + h); tokens of a fixed-length batch are b * Nq + i. The
+// grid covers B * Nq * Hq rows, a bound of the packed token count, which is
+// read from the device here.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdParams p) {
+  constexpr int kLanes = D / 8;
+  const long n_rows = (p.cu_seqlens != nullptr ? static_cast<long>(p.cu_seqlens[p.batch])
+                                               : static_cast<long>(p.batch) * p.nq) * p.hq;
+  const long row = (static_cast<long>(blockIdx.x) * kThreads + threadIdx.x) / kLanes;
+  const int part = threadIdx.x % kLanes;
+  float acc = 0.f;
+  if (row < n_rows) {
+    const long off = row * D + part * 8;  // Q/O/dO rows are tok * Hq + h, each D wide
+    const u32x4 a = ld16(static_cast<const u16*>(p.o) + off);
+    const u32x4 c = ld16(static_cast<const u16*>(p.dout) + off);
+    const bf16x8 ao = as_bf16x8(a), ad = as_bf16x8(c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc = __builtin_fmaf(static_cast<float>(ao[e]), static_cast<float>(ad[e]), acc);
+  }
+#pragma unroll
+  for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kLanes);
+  if (row < n_rows && part == 0) {
+    const long tok = row / p.hq;
+    const int h = static_cast<int>(row % p.hq);
+    long idx;
+    if (p.cu_seqlens != nullptr) {
+      idx = static_cast<long>(h) * p.cu_seqlens[p.batch] + tok;
+    } else {
+      const long b = tok / p.nq;
+      idx = (b * p.hq + h) * p.nq + (tok % p.nq);
+    }
+    p.dsum[idx] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p, int n_kt) {
+  using T = Tile<D>;
+  constexpr int NC = D / 16;  // 16-wide d chunks of the score contractions
+  constexpr int ND = D / 32;  // 32-row d tiles of dK^T, dV^T
+  __shared__ __attribute__((aligned(1024))) unsigned char q_st[2][T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_st[2][T::kBytes];
+  __shared__ __attribute__((aligned(16))) float lse_st[2][kTileRows];
+  __shared__ __attribute__((aligned(16))) float d_st[2][kTileRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  // Workgroup -> (key tile, batch-or-sequence, K/V head); the key tiles near
+  // the start of a sequence see the most queries under the causal mask and
+  // go first.
+  const int units = p.batch * p.hkv;
+  const int kt = static_cast<int>(blockIdx.x / units);
+  const int b = static_cast<int>(blockIdx.x % units) / p.hkv;
+  const int kvh = static_cast<int>(blockIdx.x % units) % p.hkv;
+  const int gq = p.hq / p.hkv;
+  const SeqBounds sb = seq_bounds(p, b);
+  const int k0 = kt * kBwdRows;
+  if (k0 >= sb.Lk) return;
+  const int kw0 = k0 + 32 * w;  // first key of this wave
+  const int key = kw0 + j;      // this lane's key (column of every score block)
+
+  const long qstride = static_cast<long>(p.hq) * D;
+  const long kstride = static_cast<long>(p.hkv) * D;
+  const u16* kg = static_cast<const u16*>(p.k) + sb.k_tok0 * kstride + static_cast<long>(kvh) * D;
+  const u16* vg = static_cast<const u16*>(p.v) + sb.k_tok0 * kstride + static_cast<long>(kvh) * D;
+
+  // K and V of this wave's keys: the B operands of S = Q K^T and dP = dO V^T
+  // (column = key, 8 consecutive d values per lane).
+  bf16x8 kf[NC], vf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (key < sb.Lk) {
+      a = ld16(kg + static_cast<long>(key) * kstride + 16 * cc + 8 * h2);
+      c = ld16(vg + static_cast<long>(key) * kstride + 16 * cc + 8 * h2);
+    }
+    kf[cc] = as_bf16x8(a);
+    vf[cc] = as_bf16x8(c);
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int t = 0; t < ND; ++t) dk[t] = dv[t] = f32x16{};
+
+  // Query blocks: every q-head of the group, rows from the block that holds
+  // key k0 (causal) or from 0, to the end of the sequence.
+  const int qb0 = CAUSAL ? (k0 / kTileRows) * kTileRows : 0;
+  const int nqb = sb.Lq > qb0 ? (sb.Lq - qb0 + kTileRows - 1) / kTileRows : 0;
+  const int n_it = nqb * gq;
+  const float c = p.scale_log2;
+
+  auto head_of = [&](int it) { return kvh * gq + it / nqb; };
+  auto issue = [&](int it, int buf) {
+    const int h = head_of(it);
+    const int q0 = qb0 + (it % nqb) * kTileRows;
+    const u16* qg = static_cast<const u16*>(p.q) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
+    const u16* dg = static_cast<const u16*>(p.dout) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
+    issue_tile<D>(qg, qstride, q0, sb.Lq, q_st[buf], tid, w);
+    issue_tile<D>(dg, qstride, q0, sb.Lq, do_st[buf], tid, w);
+    if (w < 2) {
+      // 64 floats of LSE (wave 0) or D (wave 1): one 4-byte load per lane
+      const RowIndex ri = row_index(p, sb, b, h);
+      const float* src = (w == 0 ? p.lse : p.dsum) + ri.at(q0);
+      const int rows = min(sb.Lq - q0, kTileRows);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(src), 0, static_cast<uint32_t>(rows) * 4u, kBufferFlags);
+      float* dst = w == 0 ? lse_st[buf] : d_st[buf];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  if (n_it > 0) issue(0, 0);
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    const int q0 = qb0 + (it % nqb) * kTileRows;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block `it` landed; every wave is done with block it-1
+    if (it + 1 < n_it) issue(it + 1, buf ^ 1);
+    const unsigned char* qs = q_st[buf];
+    const unsigned char* ds_ = do_st[buf];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r0 = 32 * sub;  // tile row of this 32-row sub-block
+      const int qs0 = q0 + r0;  // its first query
+      if (qs0 >= sb.Lq) break;
+      if (CAUSAL && qs0 + 31 < kw0) continue;  // every query before every key of the wave
+      // S = Q K^T and dP = dO V^T: lane = key, register r = query qs0 + mrow(r)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qs, r0, cc, lane), kf[cc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ds_, r0, cc, lane), vf[cc], dp, 0, 0, 0);
+      }
+      // P = 2^(c s - LSE log2 e) on visible pairs, dS = P (dP - D)
+      f32x16 pr, dsr;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rr = r0 + 8 * g4 + 4 * h2;
+        const float4 l4 = *reinterpret_cast<const float4*>(&lse_st[buf][rr]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&d_st[buf][rr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          const int q = qs0 + mrow(r, h2);
+          const bool vis = q < sb.Lq && key < sb.Lk && (!CAUSAL || key <= q);
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e] * kLog2e));
+          pr[r] = vis ? pe : 0.f;
+          dsr[r] = pr[r] * (dp[r] - dvv[e]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-chunks)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 pb = pack_chunk(pr, g);
+        const bf16x8 sbv = pack_chunk(dsr, g);
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ds_, r0, t, g, lane), pb, dv[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, r0, t, g, lane), sbv, dk[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // dK = scale (dK^T)^T, dV = (dV^T)^T: lane = key, register r of d-tile t =
+  // d column 32t + mrow(r); four consecutive d values per 8-byte store.
+  if (key < sb.Lk) {
+    u16* dkg = static_cast<u16*>(p.dk) + (sb.k_tok0 + key) * kstride + static_cast<long>(kvh) * D;
+    u16* dvg = static_cast<u16*>(p.dv) + (sb.k_tok0 + key) * kstride + static_cast<long>(kvh) * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 a4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a4[e] = static_cast<__bf16>(dk[t][4 * g4 + e] * p.scale);
+          v4[e] = static_cast<__bf16>(dv[t][4 * g4 + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dkg + 32 * t + 8 * g4 + 4 * h2) = a4;
+        *reinterpret_cast<bf16x4*>(dvg + 32 * t + 8 * g4 + 4 * h2) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdParams p, int n_qt) {
+  using T = Tile<D>;
+  constexpr int NC = D / 16;
+  constexpr int ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st[2][T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st[2][T::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  // Workgroup -> (query tile, batch-or-sequence, q-head), longest causal
+  // tiles first.
+  const int bh = p.hq * p.batch;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x / bh);
+  const int b = static_cast<int>(blockIdx.x % bh) / p.hq;
+  const int h = static_cast<int>(blockIdx.x % bh) % p.hq;
+  const int kvh = h / (p.hq / p.hkv);
+  const SeqBounds sb = seq_bounds(p, b);
+  const int q0 = qt * kBwdRows;
+  if (q0 >= sb.Lq) return;
+  const int wq0 = q0 + 32 * w;  // first query row of this wave
+  const int qrow = wq0 + j;     // this lane's query (column of every S^T block)
+
+  const long qstride = static_cast<long>(p.hq) * D;
+  const long kstride = static_cast<long>(p.hkv) * D;
+  const u16* qg = static_cast<const u16*>(p.q) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
+  const u16* dg = static_cast<const u16*>(p.dout) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
+  const u16* kg = static_cast<const u16*>(p.k) + sb.k_tok0 * kstride + static_cast<long>(kvh) * D;
+  const u16* vg = static_cast<const u16*>(p.v) + sb.k_tok0 * kstride + static_cast<long>(kvh) * D;
+
+  // Q and dO of this wave's rows: the B operands of S^T = K Q^T and
+  // dP^T = V dO^T (column = query, 8 consecutive d values per lane); the
+  // row's LSE (in base 2) and D.
+  bf16x8 qf[NC], dof[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (qrow < sb.Lq) {
+      a = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2);
+      c = ld16(dg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2);
+    }
+    qf[cc] = as_bf16x8(a);
+    dof[cc] = as_bf16x8(c);
+  }
+  const RowIndex ri = row_index(p, sb, b, h);
+  const float lse2 = qrow < sb.Lq ? p.lse[ri.at(qrow)] * kLog2e : 0.f;
+  const float drow = qrow < sb.Lq ? p.dsum[ri.at(qrow)] : 0.f;
+  const float c = p.scale_log2;
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int t = 0; t < ND; ++t) dq[t] = f32x16{};
+
+  int kend = sb.Lk;
+  if (CAUSAL) kend = min(kend, min(q0 + kBwdRows, sb.Lq));
+  const int nkb = (kend + kTileRows - 1) / kTileRows;
+  if (nkb > 0) {
+    issue_tile<D>(kg, kstride, 0, sb.Lk, k_st[0], tid, w);
+    issue_tile<D>(vg, kstride, 0, sb.Lk, v_st[0], tid, w);
+  }
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nkb) {
+      issue_tile<D>(kg, kstride, (kb + 1) * kTileRows, sb.Lk, k_st[buf ^ 1], tid, w);
+      issue_tile<D>(vg, kstride, (kb + 1) * kTileRows, sb.Lk, v_st[buf ^ 1], tid, w);
+    }
+    const unsigned char* ks = k_st[buf];
+    const unsigned char* vs = v_st[buf];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r0 = 32 * sub;
+      const int ks0 = kb * kTileRows + r0;  // first key of this 32-key sub-block
+      if (ks0 >= sb.Lk) break;
+      if (CAUSAL && ks0 > wq0 + 31) break;  // every key after every query of the wave
+      // S^T = K Q^T and dP^T = V dO^T: lane = query, register r = key ks0 + mrow(r)
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ks, r0, cc, lane), qf[cc], st, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vs, r0, cc, lane), dof[cc], dpt, 0, 0, 0);
+      }
+      f32x16 dst;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = ks0 + mrow(r, h2);
+        const bool vis = qrow < sb.Lq && kk < sb.Lk && (!CAUSAL || kk <= qrow);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -lse2));
+        dst[r] = vis ? pe * (dpt[r] - drow) : 0.f;
+      }
+      // dQ^T += K^T dS^T over the 32 keys (two 16-chunks)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 sbv = pack_chunk(dst, g);
+#pragma unroll
+        for (int t = 0; t < ND; ++t)
+          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, r0, t, g, lane), sbv, dq[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // dQ = scale (dQ^T)^T: lane = query, register r of d-tile t = d column
+  // 32t + mrow(r).
+  if (qrow < sb.Lq) {
+    u16* dqg = static_cast<u16*>(p.dq) + (sb.q_tok0 + qrow) * qstride + static_cast<long>(h) * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 a4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = static_cast<__bf16>(dq[t][4 * g4 + e] * p.scale);
+        *reinterpret_cast<bf16x4*>(dqg + 32 * t + 8 * g4 + 4 * h2) = a4;
+      }
+  }
+}
+
+}  // namespace
+
+// One object file per (head width, causal) pair, like the forward kernels.
+// An empty side launches nothing for it: with Nq == 0 the dK/dV kernel
+// still runs and writes zeros (no query sees any key), with Nk == 0 the dQ
+// kernel writes zeros.
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  const long n_rows = static_cast<long>(p.batch) * p.nq * p.hq;
+  if (n_rows > 0) {
+    const long dot_blocks = (n_rows * (D / 8) + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3(static_cast<unsigned>(dot_blocks)),
+                       dim3(kThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_qt = (p.nq + kBwdRows - 1) / kBwdRows;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>),
+                       dim3(static_cast<unsigned>(n_qt) * p.hq * p.batch), dim3(kThreads), 0,
+                       stream, p, n_qt);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+  }
+  if (p.nk > 0) {
+    const int n_kt = (p.nk + kBwdRows - 1) / kBwdRows;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>),
+                       dim3(static_cast<unsigned>(n_kt) * p.hkv * p.batch), dim3(kThreads), 0,
+                       stream, p, n_kt);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+#if !defined(FA_BF16_D) || !defined(FA_BF16_CAUSAL)
+#error "compile with -DFA_BF16_D=64|128 -DFA_BF16_CAUSAL=0|1"
+#endif
+template hipError_t launch_bwd_bf16<FA_BF16_D, (FA_BF16_CAUSAL != 0)>(const BwdParams&,
+                                                                    hipStream_t);
+
+}  // namespace fa

@@ -49,56 +49,16 @@
 #include <type_traits>
 #include <utility>
 
+#include "fa_bf16_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
 constexpr int kBR = kBf16TileRows;  // query rows per workgroup
-constexpr int kBC = 64;             // keys per K/V block
-constexpr int kThreads = 256;
+constexpr int kBC = kTileRows;      // keys per K/V block
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRaise = 16.f;      // the main loop keeps m while the block max is <= m + 16
-// Third descriptor word of a raw buffer resource on gfx9-family parts
-// (32-bit data format, no swizzle); the range check uses num_records.
-constexpr int kBufferFlags = 0x00020000;
-
-template <int D>
-struct Tile {
-  static constexpr int kUnits = D / 8;               // 16-byte units per row
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kBytes = kBC * kRowBytes;     // one K or V tile
-  static constexpr int kLoads = kBC * kUnits / kThreads;  // loads per lane per tile
-};
-
-// XOR swizzle of the 16-byte unit index within a row.
-template <int UNITS>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (UNITS == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-__device__ __forceinline__ u32x4 ld16(const u16* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// max and sum of a value with the same lane of the other half-wave
-__device__ __forceinline__ float xhalf_max(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Score MFMA (S^T tile = K operand x Q fragment), written as inline asm so
 // that the score accumulator is a VGPR (the vector unit reads it next) while
@@ -147,16 +107,6 @@ __device__ __forceinline__ f32x16 scale_via_scratch(f32x16 a, float f) {
   f32x16 r = tmp;
   asm volatile("" : "+a"(r));
   return r;
-}
-
-// Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Instruction plan of one key block for one wave (two 32-row query tiles).
@@ -209,30 +159,6 @@ struct Plan {
   }
 };
 static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
-
-// Start the loads of one 64-key tile of K or V (keys k0 .. k0+63) into LDS.
-// Each lane moves kLoads 16-byte units; a wave instruction fills 1 KiB of
-// contiguous LDS. Rows at or past Lk are outside the buffer range and are
-// written as zeros.
-template <int D>
-__device__ __forceinline__ void issue_tile(const u16* g, long stride, int k0, int Lk,
-                                           unsigned char* dst, int tid, int w) {
-  using T = Tile<D>;
-  const int rows = min(Lk - k0, kBC);
-  const uint32_t stride_b = static_cast<uint32_t>(stride * 2);
-  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(g + static_cast<long>(k0) * stride), 0, nrec, kBufferFlags);
-#pragma unroll
-  for (int it = 0; it < T::kLoads; ++it) {
-    const int u = it * kThreads + tid;
-    const int row = u / T::kUnits;
-    const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
-    const uint32_t voff = row * stride_b + gc * 16;
-    const int lds_off = (it * kThreads + w * 64) * 16;  // wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + lds_off), 16, voff, 0, 0, 0);
-  }
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))

@@ -35,6 +35,39 @@ extern template hipError_t launch_fwd_bf16<64, true>(const FwdParams&, hipStream
 extern template hipError_t launch_fwd_bf16<128, false>(const FwdParams&, hipStream_t);
 extern template hipError_t launch_fwd_bf16<128, true>(const FwdParams&, hipStream_t);
 
+// One attention-backward problem, already validated on the host.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;                // D = rowsum(dO * O), laid out like lse
+  const int32_t* cu_seqlens;  // device pointer, or nullptr for fixed length
+  int batch;
+  int hq;
+  int hkv;
+  int nq;
+  int nk;
+  int d;
+  float scale;
+  float scale_log2;           // scale * log2(e)
+  int causal;
+};
+
+// Launch the bf16 backward (D = rowsum(dO * O), then dQ, then dK and dV)
+// for head width D, causal or not; one object file per instance.
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+extern template hipError_t launch_bwd_bf16<64, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd_bf16<64, true>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd_bf16<128, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd_bf16<128, true>(const BwdParams&, hipStream_t);
+
 // Launch the float32 kernel (d in {64, 128}).
 hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);
 

@@ -1,6 +1,6 @@
 /*
- * libfa: exact tiled scaled-dot-product attention, forward pass, for AMD
- * Instinct MI355X (gfx950). C ABI.
+ * libfa: exact tiled scaled-dot-product attention, forward pass and its
+ * backward pass by recomputation, for AMD Instinct MI355X (gfx950). C ABI.
  *
  * The operation ("Softmax does not need the matrix", opening equation and
  * section "Carry the Normalizer"; "Understanding FlashAttention Pt 1:
@@ -102,6 +102,39 @@ int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O,
                 float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                 float scale, int causal, const int32_t* cu_seqlens,
                 void* stream);
+
+/*
+ * Attention backward by recomputation, bf16. The gradients of the forward
+ * function above for an upstream gradient dO ("Understanding FlashAttention
+ * Pt 1: Personal Notes", contents, section 3.6 "Backward pass: recompute
+ * instead of save"; semiaifoundry "attention-io-tiling", section
+ * Specifications and interfaces: the retained statistics and permitted
+ * recomputation serve the backward execution):
+ *
+ *     P = exp(scale Q K^T - LSE) on visible pairs (recomputed, never stored)
+ *     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+ *     dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q
+ *
+ * with the mask, grouped-query mapping and packed-sequence rules of fa_fwd;
+ * a K/V head's dK and dV are the sums over the query heads that read it.
+ *   Q, K, V    : the forward inputs (bf16, layouts as fa_fwd).
+ *   O, LSE     : what fa_fwd wrote for these inputs (LSE float32).
+ *   dO         : upstream gradient, bf16, laid out like O.
+ *   dQ, dK, dV : outputs, bf16, laid out like Q, K, V; every row of a
+ *                token that exists is written (rows that no query or key
+ *                sees get zeros). Float32 accumulation, one rounding.
+ *   Dsum       : float32 scratch laid out like LSE, owned by the caller; the
+ *                call writes D there first and reads it back.
+ *   other arguments as fa_fwd. Alignment: 16 bytes for every tensor,
+ *   including LSE and Dsum.
+ * B == 0, or Nq == Nk == 0, is a no-op. With Nq == 0 only K, V, dK, dV are
+ * used (dK = dV = 0); with Nk == 0 only the query-side buffers (dQ = 0).
+ * Errors as fa_fwd; d must be 64 or 128.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+           float* Dsum, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+           float scale, int causal, const int32_t* cu_seqlens, void* stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(int status);

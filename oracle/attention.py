@@ -355,7 +355,11 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
     dk = np.zeros((len(kv_picks), d))
     dv = np.zeros((len(kv_picks), d))
     group = hq // hkv
-    for n, (s, g, j) in enumerate(kv_picks):
+    # picks of one (sequence, K/V head) share the materialised rows
+    keys = sorted({(int(s), int(g)) for s, g, _ in kv_picks})
+    for s, g in keys:
+        sel = [n for n, (s2, g2, _) in enumerate(kv_picks) if s2 == s and g2 == g]
+        cols = np.array([kv_picks[n][2] for n in sel], dtype=np.int64)
         for h in range(g * group, (g + 1) * group):
             qh, kh, vh, doh = head(s, h)
             lq, lk = qh.shape[0], kh.shape[0]
@@ -364,7 +368,6 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
                 sc = np.where(visible_mask(r, lk, causal), scores(qh[r], kh, scale), -np.inf)
                 p, _, _ = softmax_rows(sc)
                 ds = softmax_rows_bwd(p, doh[r] @ vh.T)
-                dv[n] += p[:, j] @ doh[r]
-                dk[n] += scale * (ds[:, j] @ qh[r])
+                dv[sel] += p[:, cols].T @ doh[r]
+                dk[sel] += scale * (ds[:, cols].T @ qh[r])
     return dq, dk, dv
-

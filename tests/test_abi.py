@@ -26,7 +26,7 @@ def fa():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_fp32", "fa_status_string", "fa_last_error", "fa_version"])
+        ["fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_status_string", "fa_last_error", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -121,3 +121,62 @@ def test_attention_fwd_checks_tensors(fa):
         fa.attention_fwd(q, q, q)          # host tensors are refused
     with pytest.raises(TypeError):
         fa.attention_fwd(q.half(), q.half(), q.half())
+
+
+# fa_bwd: the same fake addresses; every buffer 16-byte aligned.
+GOOD_BWD = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, dsum=P, B=1, Hq=4, Hkv=2, Nq=8,
+                Nk=8, d=64, scale=0.125, causal=1, cu=None, stream=None)
+
+
+def _call_bwd(fa, **kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["dsum"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                     a["causal"], a["cu"], a["stream"])
+
+
+BAD_BWD = [(f"null_{n}", {n: 0}, -1) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv",
+                                                "dsum")] + [
+    (f"misaligned_{n}", {n: P + 8}, -4) for n in ("q", "k", "v", "o", "do", "dq", "dk", "dv")] + [
+    ("misaligned_lse_4", dict(lse=P + 4), -4),
+    ("misaligned_dsum_4", dict(dsum=P + 4), -4),
+    ("misaligned_cu", dict(cu=P + 2), -4),
+    ("neg_batch", dict(B=-1), -2),
+    ("neg_nq", dict(Nq=-1), -2),
+    ("hq_not_multiple", dict(Hq=6, Hkv=4), -2),
+    ("packed_nq_ne_nk", dict(cu=P, Nq=8, Nk=9), -2),
+    ("d_96", dict(d=96), -3),
+    ("scale_nan", dict(scale=math.nan), -4),
+    ("query_side_null_with_queries", dict(Nk=0, dq=0), -1),
+    ("key_side_null_with_keys", dict(Nq=0, dk=0), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_BWD, ids=[b[0] for b in BAD_BWD])
+def test_bwd_rejects_bad_arguments(fa, name, kw, status):
+    st = _call_bwd(fa, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error(), "a failing call must leave a message"
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0, Nk=0),
+                                dict(B=0, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, dsum=0),
+                                dict(Nq=0, Nk=0, cu=P)])
+def test_bwd_empty_work_is_a_noop(fa, kw):
+    assert _call_bwd(fa, **kw) == 0
+    assert fa.fa_last_error() == ""
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0, q=0, o=0, do=0, lse=0, dsum=0, dq=0),
+                                dict(Nk=0, k=0, v=0, dk=0, dv=0), dict()])
+def test_bwd_one_sided_and_full_calls_reach_the_device(fa, kw):
+    """Nq == 0 (dK = dV = 0 to write) or Nk == 0 (dQ = 0) is not a no-op:
+    with the other side's buffers absent it still passes validation and,
+    without a GPU, fails at the device check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _call_bwd(fa, **kw)
+    assert st == fa.FA_ERR_HIP, (st, fa.fa_last_error())
+
