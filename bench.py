@@ -16,7 +16,10 @@ workload on this host.
                     [--no-cpu-baseline]
 
 ``--seq-len`` replaces N of a fixed-length workload (same heads, d, mask
-and input recipe), e.g. to measure HBM traffic against N.
+and input recipe), e.g. to measure HBM traffic against N. ``--pass bwd``
+times ``fa_bwd`` (the gradients, by recomputation from the forward's LSE)
+on the same workload instead: 10*d algorithmic flops per visible pair
+(the score block again, dV, dP, dQ, dK), with a seeded dO.
 """
 from __future__ import annotations
 
@@ -63,14 +66,22 @@ def visible_pairs(lq: int, lk: int, causal: bool) -> int:
     return tri * (tri + 1) // 2 + max(0, lq - lk) * lk
 
 
-def algorithmic_flops(lens_q, lens_k, hq: int, d: int, causal: bool) -> int:
-    """4*d flops per visible pair: 2*d for q.k and 2*d for the p*v update."""
-    return sum(4 * d * hq * visible_pairs(a, b, causal) for a, b in zip(lens_q, lens_k))
+def algorithmic_flops(lens_q, lens_k, hq: int, d: int, causal: bool, per_pair: int = 4) -> int:
+    """per_pair*d flops per visible pair. Forward: 4*d (2*d for q.k and 2*d
+    for the p*v update). Backward: 10*d (q.k again, P^T dO, dO V^T, dS K,
+    dS^T Q)."""
+    return sum(per_pair * d * hq * visible_pairs(a, b, causal) for a, b in zip(lens_q, lens_k))
 
 
 def algorithmic_bytes(tq: int, tk: int, hq: int, hkv: int, d: int, elem: int) -> int:
     """Compulsory HBM bytes: read Q, K, V once, write O and the fp32 LSE."""
     return (2 * tq * hq * d + 2 * tk * hkv * d) * elem + 4 * tq * hq
+
+
+def algorithmic_bytes_bwd(tq: int, tk: int, hq: int, hkv: int, d: int, elem: int) -> int:
+    """Compulsory HBM bytes of the backward pass: read Q, K, V, O, dO and the
+    float32 LSE, write dQ, dK, dV, and write then read the float32 D."""
+    return ((4 * tq * hq * d + 4 * tk * hkv * d) * elem + 4 * tq * hq + 8 * tq * hq)
 
 
 def score_matrix_bytes(t_query: int, t_key: int, bytes_per_score: int) -> int:
@@ -117,10 +128,11 @@ def recorded_traffic():
 # CPU baseline: the oracle on a bounded sample of the workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(inp, w, budget_s: float = 12.0):
+def cpu_baseline(inp, w, budget_s: float = 12.0, do=None):
     """Time the fp64 oracle on whole (sequence, head) units of the workload
     until about ``budget_s`` seconds of CPU work, and scale to TFLOP/s with
-    the same algorithmic flop count as the GPU figure."""
+    the same algorithmic flop count as the GPU figure. With ``do`` (the
+    upstream gradient) the oracle's backward pass is timed instead."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -140,11 +152,16 @@ def cpu_baseline(inp, w, budget_s: float = 12.0):
         g = oracle.kv_head_of(h, w.hq, w.hkv)
         if inp.cu_seqlens is None:
             qs, ks, vs = inp.q[s, :, h], inp.k[s, :, g], inp.v[s, :, g]
+            dos = do[s, :, h] if do is not None else None
         else:
             lo, hi = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
             qs, ks, vs = inp.q[lo:hi, h], inp.k[lo:hi, g], inp.v[lo:hi, g]
-        oracle.attention_head(qs, ks, vs, w.scale, w.causal)
-        flops += 4 * w.d * visible_pairs(lens_q[s], lens_k[s], w.causal)
+            dos = do[lo:hi, h] if do is not None else None
+        if do is None:
+            oracle.attention_head(qs, ks, vs, w.scale, w.causal)
+        else:
+            oracle.attention_head_bwd(qs, ks, vs, dos, w.scale, w.causal)
+        flops += (4 if do is None else 10) * w.d * visible_pairs(lens_q[s], lens_k[s], w.causal)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -155,7 +172,8 @@ def cpu_baseline(inp, w, budget_s: float = 12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{done} of {len(units)} (sequence, q-head) units of the same workload, "
-                   f"full rows, fp64 numpy materialising S and P; {dt:.1f} s wall; "
+                   f"full rows, fp64 numpy materialising S and P"
+                   f"{' (gradients)' if do is not None else ''}; {dt:.1f} s wall; "
                    f"BLAS threads {threads}, host cpus {len(os.sched_getaffinity(0))}"),
     }
 
@@ -209,6 +227,8 @@ def main(argv=None):
                     help="skip reading the shader clock under load (amd-smi)")
     ap.add_argument("--cold-launches", type=int, default=5,
                     help="launches timed after writing a 512 MiB scrub buffer (cold L2/MALL)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -280,11 +300,36 @@ def main(argv=None):
     sptr = stream.cuda_stream
     cu_ptr = cu.data_ptr() if cu is not None else None
 
-    def step():
+    def fwd_step():
         st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                    B, w.hq, w.hkv, Nq, Nk, w.d, w.scale, int(w.causal), cu_ptr, sptr)
         if st != 0:
             raise RuntimeError(f"fa_fwd failed: {fa.fa_status_string(st)}: {fa.fa_last_error()}")
+
+    step = fwd_step
+    do_np = None
+    if args.which == "bwd":
+        if w.dtype != "bf16":
+            print("--pass bwd: the backward pass is bf16 only", file=sys.stderr)
+            return 2
+        # the forward outputs the backward reads, and a seeded upstream gradient
+        fwd_step()
+        x = np.random.default_rng(2000 + w.wid).standard_normal(inp.q.shape, dtype=np.float32)
+        do_bits = W.round_to_bf16_bits(x)
+        do_np = W.bf16_bits_to_f32(do_bits)
+        do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsum = torch.empty_like(lse)
+
+        def bwd_step():
+            st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           dsum.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d, w.scale, int(w.causal),
+                           cu_ptr, sptr)
+            if st != 0:
+                raise RuntimeError(f"fa_bwd failed: {fa.fa_status_string(st)}: "
+                                   f"{fa.fa_last_error()}")
+        step = bwd_step
 
     for _ in range(args.warmup):
         step()
@@ -325,10 +370,14 @@ def main(argv=None):
         sclk = sclk_under_load(step, torch.cuda.synchronize, float(np.mean(per_launch_ms)))
 
     ok = bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    if args.which == "bwd":
+        ok = ok and all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv))
 
-    flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal)
+    flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal,
+                              per_pair=10 if args.which == "bwd" else 4)
     tq, tk = sum(lens_q), sum(lens_k)
-    abytes = algorithmic_bytes(tq, tk, w.hq, w.hkv, w.d, elem)
+    abytes = (algorithmic_bytes_bwd if args.which == "bwd" else algorithmic_bytes)(
+        tq, tk, w.hq, w.hkv, w.d, elem)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(np.mean(per_launch_ms))
@@ -336,13 +385,14 @@ def main(argv=None):
     if w.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": recorded_traffic() if headline else None}
+                "traffic": recorded_traffic() if (headline and args.which == "fwd") else None}
     else:
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None}
 
     line = {
-        "metric": METRIC if headline else f"attention fwd TFLOP/s ({w.name})",
+        "metric": (METRIC if (headline and args.which == "fwd")
+                   else f"attention {args.which} TFLOP/s ({w.name})"),
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -383,7 +433,7 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget, do=do_np)
     print(json.dumps(line), flush=True)
     return 0 if ok else 3
 
