@@ -19,7 +19,10 @@ workload on this host.
 and input recipe), e.g. to measure HBM traffic against N. ``--pass bwd``
 times ``fa_bwd`` (the gradients, by recomputation from the forward's LSE)
 on the same workload instead: 10*d algorithmic flops per visible pair
-(the score block again, dV, dP, dQ, dK), with a seeded dO.
+(the score block again, dV, dP, dQ, dK), with a seeded dO. ``--pass decode``
+times ``fa_fwd_splitkv`` on a decode shape built from the workload's heads
+(``--decode-batch`` sequences, each with N cached keys and one new query
+that sees them all): HBM-bound, reported in GB/s of algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -211,6 +214,71 @@ def sclk_under_load(step, sync, launch_ms: float, seconds: float = 1.5):
 
 
 # ---------------------------------------------------------------------------
+# Decode (split-K/V) timing
+# ---------------------------------------------------------------------------
+
+def decode_main(args, fa, torch, dev):
+    """One JSON line for fa_fwd_splitkv on a decode shape: the bytes it must
+    move (K, V once, Q, O, LSE) per second, against the HBM roofline."""
+    w = W.WORKLOADS[args.workload]
+    n = args.seq_len or w.n
+    B = args.decode_batch
+    inp = W.draw(B, w.hq, w.hkv, 1, n, w.d, "bf16", 3000 + w.wid)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, w.hq, 1), dtype=torch.float32, device=dev)
+    nbytes = fa.fa_fwd_splitkv_workspace_bytes(B, w.hq, 1, w.d, args.decode_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step():
+        st = fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, w.hq, w.hkv, 1, n, w.d, w.scale, 0, None,
+                               args.decode_splits, ws.data_ptr(), nbytes, sptr)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd_splitkv failed: {fa.fa_last_error()}")
+
+    for _ in range(args.warmup):
+        step()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    ms = events[0].elapsed_time(events[-1]) / args.steps
+    abytes = algorithmic_bytes(B, B * n, w.hq, w.hkv, w.d, 2)
+    gbs = abytes / (ms * 1e-3) / 1e9
+    achieved = abytes / (float(np.mean(per)) * 1e-3) / 1e9
+    ok = bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    line = {
+        "metric": f"attention decode GB/s (split-K/V, {B} sequences x {n} keys, "
+                  f"Hq={w.hq}/Hkv={w.hkv}, d={w.d}, one query each)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode, {B} x {n} keys, GQA {w.hq}/{w.hkv}, d={w.d}",
+                   "batch": B, "hq": w.hq, "hkv": w.hkv, "seq_len": n, "head_dim": w.d,
+                   "num_splits": args.decode_splits, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "detail": {"alg_hbm_bytes": abytes,
+                   "alg_flops": algorithmic_flops([1] * B, [n] * B, w.hq, w.d, False),
+                   "launch_ms": {"mean": float(np.mean(per)), "min": float(np.min(per)),
+                                 "median": float(np.median(per))},
+                   "outputs_finite": ok, "device": torch.cuda.get_device_name(dev)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if ok else 3
+
+
+# ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
 
@@ -227,8 +295,10 @@ def main(argv=None):
                     help="skip reading the shader clock under load (amd-smi)")
     ap.add_argument("--cold-launches", type=int, default=5,
                     help="launches timed after writing a 512 MiB scrub buffer (cold L2/MALL)")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward pass")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="time the forward (default), the backward pass, or split-K/V decode")
+    ap.add_argument("--decode-batch", type=int, default=16)
+    ap.add_argument("--decode-splits", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -260,6 +330,9 @@ def main(argv=None):
         return 0
 
     import exact_io_aware_63_amd as fa
+
+    if args.which == "decode":
+        return decode_main(args, fa, torch, dev)
 
     w = W.WORKLOADS[args.workload]
     headline = args.workload == 4

@@ -48,6 +48,12 @@ _lib.fa_fwd_fp32.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_bwd.restype = ctypes.c_int
+_lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+_lib.fa_fwd_splitkv.restype = ctypes.c_int
+_lib.fa_fwd_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 5
+_lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [ctypes.c_int]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
@@ -55,8 +61,8 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_status_string", "fa_last_error",
-            "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+            "fa_status_string", "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -83,6 +89,18 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, 
     """C ``fa_bwd``: pointers are integer device addresses (or 0 / None)."""
     return _lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale,
                        int(causal), cu_seqlens, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k, num_splits,
+                   workspace, workspace_bytes, stream) -> int:
+    """C ``fa_fwd_splitkv``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+                               seqlens_k, num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:
+    """C ``fa_fwd_splitkv_workspace_bytes``."""
+    return _lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
 
 
 def fa_status_string(status: int) -> str:
@@ -209,3 +227,42 @@ def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_s
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return dq, dk, dv
+
+
+def attention_fwd_splitkv(q, k, v, *, num_splits: int, causal: bool = False, scale=None,
+                          seqlens_k=None, stream=None):
+    """Split-K/V forward (decode shapes) through the C ABI, bf16.
+
+    q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d]; ``seqlens_k`` an optional
+    int32 device tensor [B] of valid keys per entry. Allocates O, LSE and the
+    workspace with torch. Returns (O, LSE [B, Hq, Nq]).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda):
+        raise ValueError("seqlens_k must be an int32 device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                             int(bool(causal)),
+                             seqlens_k.data_ptr() if seqlens_k is not None else None,
+                             int(num_splits), ws.data_ptr(), nbytes, stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return o, lse

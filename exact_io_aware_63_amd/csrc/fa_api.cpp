@@ -226,6 +226,73 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   return FA_OK;
 }
 
+constexpr int kMaxSplits = 1024;
+constexpr int kDecodeRows = 32;  // query rows of one K/V head's group per split workgroup
+
+size_t decode_workspace(int B, int Hq, int Nq, int d, int n_splits) {
+  const size_t rows = static_cast<size_t>(B) * Hq * Nq * n_splits;
+  const size_t o_bytes = rows * d * 4;
+  return ((o_bytes + 255) / 256) * 256 + rows * 4;
+}
+
+int run_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+                int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+                int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B=%d, Nq=%d, Nk=%d must be >= 0", B, Nq, Nk);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_SHAPE, "Hq=%d and Hkv=%d must be > 0", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head width d=%d; supported: 64, 128", d);
+  if (static_cast<long>(Hq / Hkv) * Nq > kDecodeRows)
+    return fail(FA_ERR_UNSUPPORTED,
+                "(Hq/Hkv) * Nq = %d query rows per K/V head; the split-K/V path takes at most %d "
+                "(use fa_fwd for longer query blocks)", (Hq / Hkv) * Nq, kDecodeRows);
+  if (n_splits < 1 || n_splits > kMaxSplits)
+    return fail(FA_ERR_ARG, "num_splits=%d must be in 1..%d", n_splits, kMaxSplits);
+  if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (!Q || !O || !LSE || !workspace || (Nk > 0 && (!K || !V)))
+    return fail(FA_ERR_NULL, "Q, O, LSE, workspace (and K, V when Nk > 0) must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(workspace, 256))
+    return fail(FA_ERR_ARG, "Q, K, V and O must be 16-byte aligned, workspace 256-byte aligned");
+  if (!aligned(LSE, 4) || (seqlens_k && !aligned(seqlens_k, 4)))
+    return fail(FA_ERR_ARG, "LSE and seqlens_k must be 4-byte aligned");
+  const size_t need = decode_workspace(B, Hq, Nq, d, n_splits);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_ARG, "workspace of %zu bytes; %zu needed", workspace_bytes, need);
+  if (static_cast<long>(B) * Hkv * n_splits > 0x7fffffffL)
+    return fail(FA_ERR_SHAPE, "grid exceeds the launch limit");
+  int st = check_device();
+  if (st != FA_OK) return st;
+  fa::DecodeParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.seqlens_k = seqlens_k;
+  const size_t rows = static_cast<size_t>(B) * Hq * Nq * n_splits;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        ((rows * d * 4 + 255) / 256) * 256);
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.d = d;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.causal = causal ? 1 : 0;
+  p.n_splits = n_splits;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = d == 64 ? fa::launch_decode_bf16<64>(p, s) : fa::launch_decode_bf16<128>(p, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,6 +315,19 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            void* stream) {
   return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
                  cu_seqlens, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0 || num_splits <= 0) return 0;
+  return decode_workspace(B, Hq, Nq, d, num_splits);
+}
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   const int32_t* seqlens_k, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run_splitkv(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k, num_splits,
+                     workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

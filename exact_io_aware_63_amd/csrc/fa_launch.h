@@ -68,6 +68,33 @@ extern template hipError_t launch_bwd_bf16<64, true>(const BwdParams&, hipStream
 extern template hipError_t launch_bwd_bf16<128, false>(const BwdParams&, hipStream_t);
 extern template hipError_t launch_bwd_bf16<128, true>(const BwdParams&, hipStream_t);
 
+// One split-K/V (decode) forward problem, already validated on the host.
+struct DecodeParams {
+  const void* q;              // [B, Nq, Hq, d] bf16
+  const void* k;              // [B, Nk, Hkv, d] bf16
+  const void* v;
+  void* o;                    // [B, Nq, Hq, d] bf16
+  float* lse;                 // [B, Hq, Nq]
+  const int32_t* seqlens_k;   // device int32 [B] (keys of each entry), or nullptr: Nk
+  float* part_o;              // workspace: [n_splits, B, Hq, Nq, d] float32
+  float* part_lse;            // workspace: [n_splits, B, Hq, Nq] float32
+  int batch;
+  int hq;
+  int hkv;
+  int nq;
+  int nk;
+  int d;
+  float scale_log2;
+  int causal;
+  int n_splits;
+};
+
+// Split pass then combine pass, head width D.
+template <int D>
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+extern template hipError_t launch_decode_bf16<64>(const DecodeParams&, hipStream_t);
+extern template hipError_t launch_decode_bf16<128>(const DecodeParams&, hipStream_t);
+
 // Launch the float32 kernel (d in {64, 128}).
 hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);
 

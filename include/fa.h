@@ -63,6 +63,7 @@
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -135,6 +136,40 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
            float* Dsum, int B, int Hq, int Hkv, int Nq, int Nk, int d,
            float scale, int causal, const int32_t* cu_seqlens, void* stream);
+
+/*
+ * Split-K/V attention forward for decode-shaped problems, bf16: the same
+ * function as fa_fwd (fixed-length layout, same mask and grouping) for few
+ * query rows per head and a long K/V cache ("Understanding FlashAttention
+ * Pt 1: Personal Notes", contents, section 8.1: prefill and decode are
+ * different regimes). The keys of every (batch entry, K/V head) are cut into
+ * num_splits ranges; each range yields a softmax-normalised partial output
+ * and its log-sum-exp, and a second pass merges them with the block merge
+ * rule of "Softmax does not need the matrix", section "Carry the
+ * Normalizer": LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *   Q, O       : [B, Nq, Hq, d] bf16; K, V : [B, Nk, Hkv, d] bf16 (a cache
+ *                with room for Nk keys per batch entry); LSE : [B, Hq, Nq].
+ *   seqlens_k  : NULL (every entry has Nk keys) or device int32 [B], the
+ *                number of valid keys of each entry (clamped to 0 .. Nk);
+ *                keys past it are never read.
+ *   causal     : top-left mask as fa_fwd (query i sees keys j <= i); for
+ *                one new token attending to a whole cache pass 0.
+ *   num_splits : 1 .. 1024 key ranges per (batch entry, K/V head).
+ *   workspace  : device memory of at least
+ *                fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+ *                bytes, 256-byte aligned, owned by the caller (partial O
+ *                and LSE of every split); its contents on return are
+ *                unspecified.
+ * (Hq / Hkv) * Nq must be at most 32: the query rows of one K/V head's group
+ * form one tile (FA_ERR_UNSUPPORTED otherwise; use fa_fwd). B == 0 or
+ * Nq == 0 is a no-op. Other arguments and errors as fa_fwd.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O,
+                   float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   float scale, int causal, const int32_t* seqlens_k,
+                   int num_splits, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(int status);

@@ -26,7 +26,8 @@ def fa():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_status_string", "fa_last_error", "fa_version"])
+        ["fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+         "fa_status_string", "fa_last_error", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -179,4 +180,65 @@ def test_bwd_one_sided_and_full_calls_reach_the_device(fa, kw):
         pytest.skip("a GPU is present")
     st = _call_bwd(fa, **kw)
     assert st == fa.FA_ERR_HIP, (st, fa.fa_last_error())
+
+
+# fa_fwd_splitkv
+def _ws(B=2, Hq=8, Nq=1, d=64, n=4):
+    rows = B * Hq * Nq * n
+    return (rows * d * 4 + 255) // 256 * 256 + rows * 4
+
+
+def test_splitkv_workspace_size(fa):
+    assert fa.fa_fwd_splitkv_workspace_bytes(2, 8, 1, 64, 4) == _ws()
+    assert fa.fa_fwd_splitkv_workspace_bytes(3, 32, 2, 128, 7) == _ws(3, 32, 2, 128, 7)
+    assert fa.fa_fwd_splitkv_workspace_bytes(0, 8, 1, 64, 4) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(2, 8, 1, 64, 0) == 0
+
+
+GOOD_SKV = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, Nk=100, d=64, scale=0.125,
+                causal=0, seqlens=None, n=4, ws=P * 16, wsb=_ws(), stream=None)
+
+
+def _call_skv(fa, **kw):
+    a = dict(GOOD_SKV)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["seqlens"], a["n"],
+                             a["ws"], a["wsb"], a["stream"])
+
+
+BAD_SKV = [
+    ("null_q", dict(q=0), -1), ("null_k", dict(k=0), -1), ("null_o", dict(o=0), -1),
+    ("null_lse", dict(lse=0), -1), ("null_ws", dict(ws=0), -1),
+    ("neg_nk", dict(Nk=-1), -2), ("hq_not_multiple", dict(Hq=6, Hkv=4), -2),
+    ("d_96", dict(d=96), -3),
+    ("too_many_rows", dict(Hq=16, Hkv=1, Nq=3), -3),
+    ("zero_splits", dict(n=0), -4), ("too_many_splits", dict(n=1025), -4),
+    ("scale_nan", dict(scale=math.nan), -4),
+    ("workspace_short", dict(wsb=_ws() - 1), -4),
+    ("misaligned_ws", dict(ws=P * 16 + 16), -4),
+    ("misaligned_q", dict(q=P + 8), -4),
+    ("misaligned_seqlens", dict(seqlens=P + 2), -4),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_SKV, ids=[b[0] for b in BAD_SKV])
+def test_splitkv_rejects_bad_arguments(fa, name, kw, status):
+    st = _call_skv(fa, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0)])
+def test_splitkv_empty_work_is_a_noop(fa, kw):
+    assert _call_skv(fa, **kw) == 0
+    assert fa.fa_last_error() == ""
+
+
+def test_splitkv_valid_call_without_gpu_fails_cleanly(fa):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_skv(fa) == fa.FA_ERR_HIP
+    assert _call_skv(fa, Nk=0, k=0, v=0) == fa.FA_ERR_HIP  # no keys: O = 0, LSE = -inf to write
 
