@@ -74,19 +74,32 @@ def kv_head_of(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def visible_mask(rows: np.ndarray, lk: int, causal: bool) -> np.ndarray:
+def visible_mask(rows: np.ndarray, lk: int, causal: bool, window=None) -> np.ndarray:
     """Boolean [len(rows), lk]: True where query ``rows[r]`` may see key j.
 
     Causal reading: top-left lower-triangular, j <= i, indices local to the
     sequence ("Understanding FlashAttention Pt 1", section 3.5 title, causal
     masking; the body of that section is not in the pages, so the plain
     lower-triangular mask is taken).
+
+    ``window`` = (left, right), a sliding (local) window: query i also sees
+    only keys i - left <= j <= i + right, a negative bound meaning unbounded.
+    Reading: the pages name local attention and sliding windows only
+    ("Understanding FlashAttention Pt 1", contents, section 4.2 title;
+    "Softmax does not need the matrix", *Quadratic Time Did Not Vanish*), so
+    the plain band around the diagonal is taken, combined with the causal
+    mask by AND.
     """
     j = np.arange(lk)[None, :]
     i = np.asarray(rows)[:, None]
-    if causal:
-        return j <= i
-    return np.broadcast_to(j >= 0, (len(rows), lk))
+    m = (j <= i) if causal else np.broadcast_to(j >= 0, (len(rows), lk))
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            m = m & (j >= i - left)
+        if right >= 0:
+            m = m & (j <= i + right)
+    return m
 
 
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
@@ -116,7 +129,7 @@ def softmax_rows(s: np.ndarray):
 
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   causal: bool, rows=None):
+                   causal: bool, rows=None, window=None):
     """One (sequence, head) of attention: q [Lq, d], k and v [Lk, d].
 
     Forms S, then P, then O = P V for the selected query rows (all rows if
@@ -134,7 +147,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     for c0 in range(0, len(rows), ROW_CHUNK):
         r = rows[c0:c0 + ROW_CHUNK]
         s = scores(q[r], k, scale)                                # write S
-        s = np.where(visible_mask(r, lk, causal), s, -np.inf)
+        s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, m, l = softmax_rows(s)                                 # write P
         out[c0:c0 + len(r)] = p @ v                               # O = P V
         with np.errstate(divide="ignore"):
@@ -142,7 +155,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return out, lse
 
 
-def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None):
+def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None, window=None):
     """Full forward pass in the token-major layouts of the module docstring.
 
     Returns (O, LSE) as float64 arrays.
@@ -158,7 +171,8 @@ def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None):
         for b in range(bsz):
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
-                o_bh, l_bh = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal)
+                o_bh, l_bh = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal,
+                                            window=window)
                 out[b, :, h] = o_bh
                 lse[b, h] = l_bh
         return out, lse
@@ -171,13 +185,14 @@ def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None):
         lo, hi = int(cu[s]), int(cu[s + 1])
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
-            o_sh, l_sh = attention_head(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], scale, causal)
+            o_sh, l_sh = attention_head(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], scale, causal,
+                                        window=window)
             out[lo:hi, h] = o_sh
             lse[h, lo:hi] = l_sh
     return out, lse
 
 
-def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None):
+def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None, window=None):
     """Selected outputs only, one (batch-or-sequence, q-head, row) at a time.
 
     For parity checks at sizes where the full oracle would take too long:
@@ -215,7 +230,8 @@ def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None
         o_sel, l_sel = attention_head(np.asarray(qs, dtype=np.float64),
                                       np.asarray(ks, dtype=np.float64),
                                       np.asarray(vs, dtype=np.float64),
-                                      scale, causal, rows=picks[sel, 2])
+                                      scale, causal, rows=picks[sel, 2],
+                                      window=window)
         out[sel] = o_sel
         lse[sel] = l_sel
         i0 = i1
@@ -238,7 +254,7 @@ def softmax_rows_bwd(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
     return p * (dp - (p * dp).sum(axis=1, keepdims=True))
 
 
-def attention_head_bwd(q, k, v, do, scale: float, causal: bool):
+def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None):
     """Gradients of one (sequence, head): q, do [Lq, d]; k, v [Lk, d].
 
     Forms S = scale q K^T, the mask, P = softmax_row(S) (as the forward
@@ -260,7 +276,7 @@ def attention_head_bwd(q, k, v, do, scale: float, causal: bool):
     for c0 in range(0, lq, ROW_CHUNK):
         r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
         s = scores(q[r], k, scale)
-        s = np.where(visible_mask(r, lk, causal), s, -np.inf)
+        s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, _, _ = softmax_rows(s)
         dv += p.T @ do[r]
         dp = do[r] @ v.T
@@ -270,7 +286,7 @@ def attention_head_bwd(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
-def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None):
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, window=None):
     """Gradients in the layouts of the module docstring (dO like O).
 
     Returns (dQ like q, dK like k, dV like v) as float64 arrays. With
@@ -291,7 +307,7 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None):
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
                 a, bk, bv = attention_head_bwd(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h],
-                                               scale, causal)
+                                               scale, causal, window=window)
                 dq[b, :, h] = a
                 dk[b, :, g] += bk
                 dv[b, :, g] += bv
@@ -303,7 +319,7 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None):
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             a, bk, bv = attention_head_bwd(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], do[lo:hi, h],
-                                           scale, causal)
+                                           scale, causal, window=window)
             dq[lo:hi, h] = a
             dk[lo:hi, g] += bk
             dv[lo:hi, g] += bv
@@ -311,7 +327,7 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None):
 
 
 def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_picks,
-                         cu_seqlens=None):
+                         cu_seqlens=None, window=None):
     """Selected gradient rows, for parity checks at sizes where the full
     oracle would take too long.
 
@@ -348,7 +364,8 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
     for n, (s, h, i) in enumerate(q_picks):
         qh, kh, vh, doh = head(s, h)
         r = np.array([i])
-        sc = np.where(visible_mask(r, kh.shape[0], causal), scores(qh[r], kh, scale), -np.inf)
+        sc = np.where(visible_mask(r, kh.shape[0], causal, window), scores(qh[r], kh, scale),
+                      -np.inf)
         p, _, _ = softmax_rows(sc)
         ds = softmax_rows_bwd(p, doh[r] @ vh.T)
         dq[n] = scale * (ds @ kh)[0]
@@ -365,7 +382,8 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
             lq, lk = qh.shape[0], kh.shape[0]
             for c0 in range(0, lq, ROW_CHUNK):
                 r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
-                sc = np.where(visible_mask(r, lk, causal), scores(qh[r], kh, scale), -np.inf)
+                sc = np.where(visible_mask(r, lk, causal, window), scores(qh[r], kh, scale),
+                              -np.inf)
                 p, _, _ = softmax_rows(sc)
                 ds = softmax_rows_bwd(p, doh[r] @ vh.T)
                 dv[sel] += p[:, cols].T @ doh[r]

@@ -268,9 +268,33 @@ def pin_bwd_empty_and_zero_upstream():
     assert dk.shape == (1, 0, 1, 3) and dv.shape == (1, 0, 1, 3)
 
 
+def pin_bwd_window_finite_differences():
+    """Gradients with a sliding window (causal and not) against central
+    differences of the windowed forward oracle."""
+    rng = _rng(112)
+    for causal, win in ((True, (3, -1)), (False, (2, 1))):
+        q = rng.standard_normal((1, 10, 2, 4))
+        k = rng.standard_normal((1, 10, 1, 4))
+        v = rng.standard_normal((1, 10, 1, 4))
+        do = rng.standard_normal((1, 10, 2, 4))
+        dq, dk, dv = A.attention_bwd_ref(q, k, v, do, 0.6, causal, window=win)
+
+        def loss(qq, kk, vv):
+            return float((A.attention_ref(qq, kk, vv, 0.6, causal, window=win)[0] * do).sum())
+
+        for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            e = rng.standard_normal(x.shape)
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[which] = x + FD_EPS * e
+            args_m[which] = x - FD_EPS * e
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * FD_EPS)
+            _assert_close(float((g * e).sum()), fd, FD_TOL * max(1.0, abs(fd)),
+                          f"window directional {'QKV'[which]}")
+
+
 ALL_BWD_PINS = [
     pin_bwd_finite_differences, pin_bwd_elementwise_numeric_gradient, pin_bwd_single_key,
     pin_bwd_zero_scale, pin_bwd_key_translation, pin_bwd_dv_column_sum,
     pin_bwd_gqa_is_repeated_heads, pin_bwd_packed_is_independent, pin_bwd_library_autograd,
-    pin_bwd_picked_rows, pin_bwd_empty_and_zero_upstream,
+    pin_bwd_picked_rows, pin_bwd_empty_and_zero_upstream, pin_bwd_window_finite_differences,
 ]

@@ -424,9 +424,83 @@ def pin_picked_rows():
         _assert_close(pl[r], lse[h, cu[s] + i], 1e-15, "picked packed LSE")
 
 
+def pin_window_wide_equals_plain():
+    """A window wider than the sequence changes nothing."""
+    rng = _rng(31)
+    q = rng.standard_normal((2, 9, 2, 4))
+    k = rng.standard_normal((2, 11, 1, 4))
+    v = rng.standard_normal((2, 11, 1, 4))
+    for causal in (False, True):
+        o, lse = A.attention_ref(q, k, v, 0.6, causal)
+        ow, lw = A.attention_ref(q, k, v, 0.6, causal, window=(100, 100))
+        _assert_close(ow, o, 0.0, "wide window O")
+        _assert_close(lw, lse, 0.0, "wide window LSE")
+        ow, lw = A.attention_ref(q, k, v, 0.6, causal, window=(-1, -1))
+        _assert_close(ow, o, 0.0, "unbounded window O")
+
+
+def pin_window_zero_left_causal():
+    """Left window 0 under the causal mask: row i sees key i only, so
+    O_i = v_i and LSE_i = scale * q_i . k_i."""
+    rng = _rng(32)
+    q = rng.standard_normal((1, 7, 1, 5))
+    k = rng.standard_normal((1, 7, 1, 5))
+    v = rng.standard_normal((1, 7, 1, 5))
+    o, lse = A.attention_ref(q, k, v, 0.8, True, window=(0, -1))
+    _assert_close(o, v, 1e-15, "zero left window O")
+    want = 0.8 * np.einsum("bihd,bihd->bhi", q, k)
+    _assert_close(lse, want, 1e-14, "zero left window LSE")
+
+
+def pin_window_by_slicing():
+    """Each row of a windowed call equals the unmasked oracle over that
+    row's own key slice [i - left, i + right] (cut at 0, Lk and, causal, at
+    i): slicing instead of masking, a different route."""
+    rng = _rng(33)
+    lq, lk, d = 12, 10, 4
+    q = rng.standard_normal((lq, d))
+    k = rng.standard_normal((lk, d))
+    v = rng.standard_normal((lk, d))
+    for causal, win in ((False, (2, 3)), (True, (3, -1)), (False, (0, 0)), (True, (1, 5)),
+                        (False, (-1, 1))):
+        o, lse = A.attention_head(q, k, v, 0.7, causal, window=win)
+        for i in range(lq):
+            lo = 0 if win[0] < 0 else max(0, i - win[0])
+            hi = lk if win[1] < 0 else min(lk, i + win[1] + 1)
+            if causal:
+                hi = min(hi, i + 1)
+            if hi <= lo:
+                assert np.all(o[i] == 0) and np.isneginf(lse[i]), "empty window row"
+                continue
+            oi, li = A.attention_head(q[i:i + 1], k[lo:hi], v[lo:hi], 0.7, False)
+            _assert_close(o[i], oi[0], 1e-14, f"window row {i} O")
+            _assert_close(lse[i], li[0], 1e-14, f"window row {i} LSE")
+
+
+def pin_window_brute_force():
+    """Pure-Python per-row evaluation over the explicit key range."""
+    rng = _rng(34)
+    q = rng.standard_normal((6, 3))
+    k = rng.standard_normal((8, 3))
+    v = rng.standard_normal((8, 3))
+    o, lse = A.attention_head(q, k, v, 0.9, True, window=(2, -1))
+    for i in range(6):
+        keys = [j for j in range(8) if i - 2 <= j <= i]
+        s = [0.9 * math.fsum(q[i, c] * k[j, c] for c in range(3)) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        den = math.fsum(e)
+        for c in range(3):
+            _assert_close(o[i, c], math.fsum(e[n] * v[keys[n], c] for n in range(len(keys))) / den,
+                          1e-13, "window brute-force O")
+        _assert_close(lse[i], m + math.log(den), 1e-13, "window brute-force LSE")
+
+
 ALL_PINS = [
     pin_rows_sum_to_one, pin_single_key, pin_uniform_scores_mean, pin_two_key_closed_form,
     pin_permutation_invariance, pin_brute_force, pin_online_route, pin_causal_structure,
     pin_gqa_is_repeated_heads, pin_packed_is_independent, pin_shift_invariance,
     pin_hard_max_limit, pin_library_sdpa, pin_empty_cases, pin_picked_rows,
+    pin_window_wide_equals_plain, pin_window_zero_left_causal, pin_window_by_slicing,
+    pin_window_brute_force,
 ]

@@ -18,7 +18,7 @@ _orig_head_bwd = A.attention_head_bwd
 
 def _head_bwd_variant(change):
     """The oracle's per-head gradient steps with one planted change."""
-    def f(q, k, v, do, scale, causal):
+    def f(q, k, v, do, scale, causal, window=None):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
         lq, lk = q.shape[0], k.shape[0]
         dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -27,7 +27,7 @@ def _head_bwd_variant(change):
         r = np.arange(lq)
         s = A.scores(q, k, scale)
         if change != "mask_ignored":
-            s = np.where(A.visible_mask(r, lk, causal), s, -np.inf)
+            s = np.where(A.visible_mask(r, lk, causal, window), s, -np.inf)
         p, _, _ = A.softmax_rows(s)
         dp = do @ v.T
         ds = A.softmax_rows_bwd(p, dp)
@@ -40,7 +40,7 @@ def _head_bwd_variant(change):
     return f
 
 
-def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None):
+def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None, window=None):
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     if cu_seqlens is None:

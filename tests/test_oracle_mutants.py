@@ -13,6 +13,7 @@ from oracle_pins import ALL_PINS
 
 _orig_head = A.attention_head
 _orig_softmax = A.softmax_rows
+_orig_visible = A.visible_mask
 
 
 def _softmax_no_max(s):
@@ -34,23 +35,51 @@ def _softmax_lse_no_l(s):
     return p, m, np.ones_like(l)
 
 
-def _visible_strict(rows, lk, causal):
+def _visible_strict(rows, lk, causal, window=None):
     j = np.arange(lk)[None, :]
     i = np.asarray(rows)[:, None]
     return (j < i) if causal else np.broadcast_to(j >= 0, (len(rows), lk))
 
 
-def _visible_reversed(rows, lk, causal):
+def _visible_reversed(rows, lk, causal, window=None):
     j = np.arange(lk)[None, :]
     i = np.asarray(rows)[:, None]
     return (j >= i) if causal else np.broadcast_to(j >= 0, (len(rows), lk))
 
 
-def _visible_ignores_causal(rows, lk, causal):
+def _visible_ignores_causal(rows, lk, causal, window=None):
     return np.broadcast_to(np.arange(lk)[None, :] >= 0, (len(rows), lk))
 
 
+def _window_left_off_by_one(rows, lk, causal, window=None):
+    m = _orig_visible(rows, lk, causal, None)
+    if window is not None:
+        j = np.arange(lk)[None, :]
+        i = np.asarray(rows)[:, None]
+        if window[0] >= 0:
+            m = m & (j > i - window[0])
+        if window[1] >= 0:
+            m = m & (j <= i + window[1])
+    return m
+
+
+def _window_right_off_by_one(rows, lk, causal, window=None):
+    m = _orig_visible(rows, lk, causal, None)
+    if window is not None:
+        j = np.arange(lk)[None, :]
+        i = np.asarray(rows)[:, None]
+        if window[0] >= 0:
+            m = m & (j >= i - window[0])
+        if window[1] >= 0:
+            m = m & (j < i + window[1])
+    return m
+
+
 MUTANTS = {
+    "window_ignored": ("visible_mask", lambda rows, lk, causal, window=None:
+                       _orig_visible(rows, lk, causal, None)),
+    "window_left_off_by_one": ("visible_mask", _window_left_off_by_one),
+    "window_right_off_by_one": ("visible_mask", _window_right_off_by_one),
     "gqa_modulo_grouping": ("kv_head_of", lambda h, hq, hkv: h % hkv),
     "causal_strict_lower": ("visible_mask", _visible_strict),
     "causal_reversed": ("visible_mask", _visible_reversed),
@@ -61,17 +90,19 @@ MUTANTS = {
     "softmax_wrong_axis": ("softmax_rows", _softmax_wrong_axis),
     "lse_without_denominator": ("softmax_rows", _softmax_lse_no_l),
     "values_are_keys": ("attention_head",
-                        lambda q, k, v, scale, causal, rows=None: _orig_head(q, k, k, scale, causal, rows)),
+                        lambda q, k, v, scale, causal, rows=None, window=None:
+                        _orig_head(q, k, k, scale, causal, rows, window)),
     "lse_log2": ("attention_head",
-                 lambda q, k, v, scale, causal, rows=None:
-                 (lambda o, l: (o, l / np.log(2.0)))(*_orig_head(q, k, v, scale, causal, rows))),
+                 lambda q, k, v, scale, causal, rows=None, window=None:
+                 (lambda o, l: (o, l / np.log(2.0)))(*_orig_head(q, k, v, scale, causal, rows,
+                                                                 window))),
     "last_key_dropped": ("attention_head",
-                         lambda q, k, v, scale, causal, rows=None:
-                         _orig_head(q, k[:-1], v[:-1], scale, causal, rows)),
+                         lambda q, k, v, scale, causal, rows=None, window=None:
+                         _orig_head(q, k[:-1], v[:-1], scale, causal, rows, window)),
     "first_row_skipped": ("attention_head",
-                          lambda q, k, v, scale, causal, rows=None:
+                          lambda q, k, v, scale, causal, rows=None, window=None:
                           (lambda o, l: (np.concatenate([np.zeros_like(o[:1]), o[1:]]), l))(
-                              *_orig_head(q, k, v, scale, causal, rows))),
+                              *_orig_head(q, k, v, scale, causal, rows, window))),
 }
 
 
