@@ -61,19 +61,32 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_bf16_causal_gqa_n8
 # Work and bytes model (host arithmetic, no attention math)
 # ---------------------------------------------------------------------------
 
-def visible_pairs(lq: int, lk: int, causal: bool) -> int:
-    """Visible (query, key) pairs of one head; top-left causal mask."""
-    if not causal:
-        return lq * lk
-    tri = min(lq, lk)
-    return tri * (tri + 1) // 2 + max(0, lq - lk) * lk
+def visible_pairs(lq: int, lk: int, causal: bool, window=None) -> int:
+    """Visible (query, key) pairs of one head; top-left causal mask, and an
+    optional sliding window (left, right), negative = unbounded."""
+    if window is None or (window[0] < 0 and window[1] < 0):
+        if not causal:
+            return lq * lk
+        tri = min(lq, lk)
+        return tri * (tri + 1) // 2 + max(0, lq - lk) * lk
+    left, right = window
+    i = np.arange(lq, dtype=np.int64)
+    lo = np.zeros(lq, dtype=np.int64) if left < 0 else np.maximum(0, i - left)
+    hi = np.full(lq, lk - 1, dtype=np.int64)
+    if right >= 0:
+        hi = np.minimum(hi, i + right)
+    if causal:
+        hi = np.minimum(hi, i)
+    return int(np.maximum(0, hi - lo + 1).sum())
 
 
-def algorithmic_flops(lens_q, lens_k, hq: int, d: int, causal: bool, per_pair: int = 4) -> int:
+def algorithmic_flops(lens_q, lens_k, hq: int, d: int, causal: bool, per_pair: int = 4,
+                      window=None) -> int:
     """per_pair*d flops per visible pair. Forward: 4*d (2*d for q.k and 2*d
     for the p*v update). Backward: 10*d (q.k again, P^T dO, dO V^T, dS K,
     dS^T Q)."""
-    return sum(per_pair * d * hq * visible_pairs(a, b, causal) for a, b in zip(lens_q, lens_k))
+    return sum(per_pair * d * hq * visible_pairs(a, b, causal, window)
+               for a, b in zip(lens_q, lens_k))
 
 
 def algorithmic_bytes(tq: int, tk: int, hq: int, hkv: int, d: int, elem: int) -> int:
@@ -297,6 +310,9 @@ def main(argv=None):
                     help="launches timed after writing a 512 MiB scrub buffer (cold L2/MALL)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="time the forward (default), the backward pass, or split-K/V decode")
+    ap.add_argument("--window", type=int, default=-1, metavar="LEFT",
+                    help="forward with a sliding window of LEFT keys before each query "
+                         "(fa_fwd_window; bf16)")
     ap.add_argument("--decode-batch", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,6 +395,17 @@ def main(argv=None):
         if st != 0:
             raise RuntimeError(f"fa_fwd failed: {fa.fa_status_string(st)}: {fa.fa_last_error()}")
 
+    if args.window >= 0 and args.which == "fwd":
+        if w.dtype != "bf16":
+            print("--window needs a bf16 workload", file=sys.stderr)
+            return 2
+
+        def fwd_step():  # noqa: F811  (the windowed forward replaces the plain one)
+            st = fa.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d, w.scale,
+                                  int(w.causal), args.window, -1, cu_ptr, sptr)
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_window failed: {fa.fa_last_error()}")
     step = fwd_step
     do_np = None
     if args.which == "bwd":
@@ -446,8 +473,11 @@ def main(argv=None):
     if args.which == "bwd":
         ok = ok and all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv))
 
+    win = (args.window, -1) if (args.window >= 0 and args.which == "fwd") else None
     flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal,
-                              per_pair=10 if args.which == "bwd" else 4)
+                              per_pair=10 if args.which == "bwd" else 4, window=win)
+    if win is not None:
+        headline = False
     tq, tk = sum(lens_q), sum(lens_k)
     abytes = (algorithmic_bytes_bwd if args.which == "bwd" else algorithmic_bytes)(
         tq, tk, w.hq, w.hkv, w.d, elem)
@@ -465,7 +495,8 @@ def main(argv=None):
 
     line = {
         "metric": (METRIC if (headline and args.which == "fwd")
-                   else f"attention {args.which} TFLOP/s ({w.name})"),
+                   else f"attention {args.which} TFLOP/s ({w.name}"
+                        f"{f', window {args.window}' if win is not None else ''})"),
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -45,6 +45,10 @@ _lib.fa_fwd.argtypes = _FWD_ARGS
 _lib.fa_fwd.restype = ctypes.c_int
 _lib.fa_fwd_fp32.argtypes = _FWD_ARGS
 _lib.fa_fwd_fp32.restype = ctypes.c_int
+_lib.fa_fwd_window.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                               [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p])
+_lib.fa_fwd_window.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_bwd.restype = ctypes.c_int
@@ -61,7 +65,7 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
             "fa_status_string", "fa_last_error", "fa_version")
 
 
@@ -82,6 +86,13 @@ def fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlen
     """C ``fa_fwd_fp32``: pointers are integer device addresses (or 0 / None)."""
     return _lib.fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
                             cu_seqlens, stream)
+
+
+def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left, window_right,
+                  cu_seqlens, stream) -> int:
+    """C ``fa_fwd_window``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+                              window_left, window_right, cu_seqlens, stream)
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
@@ -116,13 +127,14 @@ def fa_version() -> int:
 
 
 def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
-                  max_seqlen=None, out=None, lse=None, stream=None):
+                  max_seqlen=None, out=None, lse=None, stream=None, window=None):
     """Attention forward on torch device tensors through the C ABI.
 
     Fixed length: q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d].
     Packed: q [T, Hq, d], k and v [T, Hkv, d], ``cu_seqlens`` int32 [nseq+1]
     on the device and ``max_seqlen`` the longest sequence (a host int).
-    bf16 tensors go to ``fa_fwd``, float32 tensors to ``fa_fwd_fp32``.
+    bf16 tensors go to ``fa_fwd``, float32 tensors to ``fa_fwd_fp32``;
+    ``window`` = (left, right) selects ``fa_fwd_window`` (bf16 only).
     Returns (O, LSE); O has q's shape and dtype, LSE is float32 [B, Hq, Nq]
     (packed: [Hq, T]).
     """
@@ -173,8 +185,15 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
         lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cu_ptr, stream)
+    if window is not None:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("a sliding window needs bfloat16 tensors")
+        st = _lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                int(bool(causal)), int(window[0]), int(window[1]), cu_ptr, stream)
+    else:
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cu_ptr, stream)
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return out, lse

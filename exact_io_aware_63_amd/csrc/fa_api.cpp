@@ -107,7 +107,7 @@ int validate(const void* Q, const void* K, const void* V, const void* O, const f
 
 int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
         int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
-        void* stream) {
+        void* stream, int win_left = -1, int win_right = -1) {
   g_last_error[0] = '\0';
   bool noop = false;
   const int tile_rows = bf16 ? fa::kBf16TileRows : fa::kFp32TileRows;
@@ -130,6 +130,8 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   p.d = d;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.causal = causal ? 1 : 0;
+  p.win_left = win_left < 0 ? -1 : win_left;
+  p.win_right = win_right < 0 ? -1 : win_right;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (!bf16)
@@ -301,6 +303,13 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
            int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
            void* stream) {
   return run(true, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream);
+}
+
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+                  int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
+                  int window_right, const int32_t* cu_seqlens, void* stream) {
+  return run(true, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream,
+             window_left, window_right);
 }
 
 int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O, float* LSE, int B,

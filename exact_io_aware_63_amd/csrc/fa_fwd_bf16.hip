@@ -160,7 +160,11 @@ struct Plan {
 };
 static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
 
-template <int D, bool CAUSAL>
+// WIN: sliding window, query i sees keys i - win_left .. i + win_right
+// (a negative bound is unbounded), on top of the causal mask. The
+// workgroup streams only the key blocks its rows' windows reach; blocks
+// are indexed from the first of them, kb_base.
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdParams p, int n_qt) {
   using T = Tile<D>;
@@ -239,15 +243,26 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // its share of every tile and meets every barrier).
   int kend = Lk;
   if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
-  const int nblk = (kend + kBC - 1) / kBC;
+  int kb_base = 0;  // first key block of the workgroup
+  if constexpr (WIN) {
+    if (p.win_right >= 0) kend = min(kend, min(q0 + kBR, Lq) - 1 + p.win_right + 1);
+    if (p.win_left >= 0) kb_base = max(0, q0 - p.win_left) / kBC;
+  }
+  const int key_base = kb_base * kBC;  // first key of local block 0
+  int nblk;
+  if constexpr (WIN) nblk = kend > key_base ? (kend + kBC - 1) / kBC - kb_base : 0;
+  else nblk = (kend + kBC - 1) / kBC;
   const int wq0 = q0 + 64 * w;  // first query row of this wave
   int nblk_w = wq0 >= Lq ? 0 : nblk;
-  if (CAUSAL) nblk_w = min(nblk_w, wq0 / kBC + 1);
+  if (CAUSAL) nblk_w = min(nblk_w, wq0 / kBC + 1 - kb_base);
+  if constexpr (WIN) {
+    if (p.win_right >= 0) nblk_w = min(nblk_w, (wq0 + 63 + p.win_right) / kBC + 1 - kb_base);
+  }
 
   if (nblk > 0) {
-    issue_tile<D>(kg, kstride, 0, Lk, kb0, tid, w);
-    issue_tile<D>(vg, kstride, 0, Lk, vb0, tid, w);
-    if (nblk > 1) issue_tile<D>(kg, kstride, kBC, Lk, kb1, tid, w);
+    issue_tile<D>(kg, kstride, key_base, Lk, kb0, tid, w);
+    issue_tile<D>(vg, kstride, key_base, Lk, vb0, tid, w);
+    if (nblk > 1) issue_tile<D>(kg, kstride, key_base + kBC, Lk, kb1, tid, w);
   }
 
   // A negative scale is applied by negating Q (exact in bf16), so that the
@@ -350,15 +365,15 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     unsigned char* v_free = PAR ? vb0 : vb1;        // V_{j-1}, consumed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (jb + 2 < nblk) issue_tile<D>(kg, kstride, (jb + 2) * kBC, Lk, k_free, tid, w);
-    if (jb + 1 < nblk) issue_tile<D>(vg, kstride, (jb + 1) * kBC, Lk, v_free, tid, w);
+    if (jb + 2 < nblk) issue_tile<D>(kg, kstride, key_base + (jb + 2) * kBC, Lk, k_free, tid, w);
+    if (jb + 1 < nblk) issue_tile<D>(vg, kstride, key_base + (jb + 1) * kBC, Lk, v_free, tid, w);
   };
   auto body = [&](auto par_tag, int jb, f32x16(&sc)[2][2], f32x16(&sn)[2][2]) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
     const unsigned char* k_next = PAR ? kb0 : kb1;  // K_{j+1}
     const unsigned char* v_cur = PAR ? vb1 : vb0;   // V_j
     if (jb >= nblk_w) return;
-    const int k0 = jb * kBC;
+    const int k0 = key_base + jb * kBC;
     mfma_result_guard();  // the last score MFMAs of sc may still be in flight
 
     // LDS operands: score operand p (K tile p/NC, d-chunk p%NC) is first used
@@ -380,16 +395,39 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     // diagonal of this wave are masked: visible iff key <= lim, with
     // key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4). c >= FLT_MIN keeps
     // 2^(c * -inf - m) = 0.
-    if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0)) {
+    if constexpr (!WIN) {
+      if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int qrow = wq0 + 32 * qt + j;
-        const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
+        for (int qt = 0; qt < 2; ++qt) {
+          const int qrow = wq0 + 32 * qt + j;
+          const int lim = (CAUSAL ? min(Lk - 1, qrow) : Lk - 1) - k0 - 4 * h2;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sc[qt][kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[qt][kt][r] : -INFINITY;
+            for (int r = 0; r < 16; ++r)
+              sc[qt][kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[qt][kt][r] : -INFINITY;
+        }
+      }
+    } else {  // also the window's edges: visible iff lim_lo <= key - k0 - 4*h2 <= lim
+      if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0) ||
+          (p.win_left >= 0 && k0 < wq0 + 63 - p.win_left) ||
+          (p.win_right >= 0 && k0 + kBC - 1 > wq0 + p.win_right)) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int qrow = wq0 + 32 * qt + j;
+          int hi = CAUSAL ? min(Lk - 1, qrow) : Lk - 1;
+          if (p.win_right >= 0) hi = min(hi, qrow + p.win_right);
+          const int lo = p.win_left >= 0 ? qrow - p.win_left : 0;
+          const int lim = hi - k0 - 4 * h2;
+          const int lim_lo = lo - k0 - 4 * h2;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int off = 32 * kt + 8 * (r >> 2) + (r & 3);
+              sc[qt][kt][r] = (off <= lim && off >= lim_lo) ? sc[qt][kt][r] : -INFINITY;
+            }
+        }
       }
     }
     float mb[2];
@@ -518,7 +556,12 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int n_qt = (p.nq + kBR - 1) / kBR;
   const unsigned grid = static_cast<unsigned>(n_qt) * p.hq * p.batch;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p, n_qt);
+  if (p.win_left >= 0 || p.win_right >= 0)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       p, n_qt);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       p, n_qt);
   return hipGetLastError();
 }
 

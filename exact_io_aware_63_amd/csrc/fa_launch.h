@@ -23,6 +23,8 @@ struct FwdParams {
   int d;
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   int causal;
+  int win_left;               // sliding window: query i sees keys >= i - win_left (-1: all)
+  int win_right;              // and keys <= i + win_right (-1: all); bf16 kernels only
 };
 
 // Launch the bf16 kernel for head width D (64 or 128), causal or not.

@@ -98,6 +98,23 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int Hq, int Hkv, int Nq, int Nk, int d,
            float scale, int causal, const int32_t* cu_seqlens, void* stream);
 
+/*
+ * fa_fwd with a sliding (local) window: query i sees only keys j with
+ * i - window_left <= j <= i + window_right (indices local to the batch entry
+ * or sequence), ANDed with the causal mask when causal != 0; a negative
+ * bound is unbounded, and with both negative the call is fa_fwd. The pages
+ * name local attention and sliding windows as variants of the mask
+ * ("Understanding FlashAttention Pt 1: Personal Notes", contents, section
+ * 4.2; "Softmax does not need the matrix", section "Quadratic Time Did Not
+ * Vanish"). Key blocks outside every window of a query tile are not read.
+ * A row whose window holds no key gets O = 0 and LSE = -inf. bf16; other
+ * arguments and errors as fa_fwd.
+ */
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O,
+                  float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                  float scale, int causal, int window_left, int window_right,
+                  const int32_t* cu_seqlens, void* stream);
+
 /* Same contract with float32 Q, K, V, O (no bf16 rounding anywhere). */
 int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O,
                 float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
