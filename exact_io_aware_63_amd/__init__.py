@@ -52,6 +52,10 @@ _lib.fa_fwd_window.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_bwd.restype = ctypes.c_int
+_lib.fa_bwd_window.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
+                               [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p])
+_lib.fa_bwd_window.restype = ctypes.c_int
 _lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
                                 [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
@@ -65,7 +69,7 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_bwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
             "fa_status_string", "fa_last_error", "fa_version")
 
 
@@ -199,8 +203,15 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
     return out, lse
 
 
+def fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                  window_left, window_right, cu_seqlens, stream) -> int:
+    """C ``fa_bwd_window``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale,
+                              int(causal), window_left, window_right, cu_seqlens, stream)
+
+
 def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_seqlens=None,
-                  max_seqlen=None, stream=None):
+                  max_seqlen=None, stream=None, window=None):
     """Gradients (dQ, dK, dV) of attention through the C ABI (bf16 only).
 
     Tensors as ``attention_fwd`` takes and returns them (``o`` and ``lse``
@@ -240,9 +251,16 @@ def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_s
     dsum = torch.empty_like(lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dsum.data_ptr(),
-                     B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), cu_ptr, stream)
+    if window is not None:
+        st = _lib.fa_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), dsum.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                int(bool(causal)), int(window[0]), int(window[1]), cu_ptr, stream)
+    else:
+        st = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         dsum.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                         cu_ptr, stream)
     if st != FA_OK:
         raise FaError(st, fa_last_error())
     return dq, dk, dv

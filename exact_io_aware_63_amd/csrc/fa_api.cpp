@@ -189,7 +189,7 @@ int validate_bwd(const void* Q, const void* K, const void* V, const void* O, con
 int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
             const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq, int Hkv,
             int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
-            void* stream) {
+            void* stream, int win_left = -1, int win_right = -1) {
   g_last_error[0] = '\0';
   bool noop = false;
   int st = validate_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale,
@@ -218,6 +218,8 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   p.scale = scale;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.causal = causal ? 1 : 0;
+  p.win_left = win_left < 0 ? -1 : win_left;
+  p.win_right = win_right < 0 ? -1 : win_right;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 64)
@@ -324,6 +326,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            void* stream) {
   return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
                  cu_seqlens, stream);
+}
+
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq,
+                  int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
+                  int window_right, const int32_t* cu_seqlens, void* stream) {
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 cu_seqlens, stream, window_left, window_right);
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {

@@ -95,6 +95,16 @@ __device__ __forceinline__ bf16x8 pack_chunk(const f32x16& x, int g) {
   return r;
 }
 
+// Key `key` visible to query `q` (sequence-local): inside both sequences,
+// under the causal mask, and inside the sliding window when WIN.
+template <bool CAUSAL, bool WIN>
+__device__ __forceinline__ bool visible(const BwdParams& p, int q, int key, int Lq, int Lk) {
+  bool v = q < Lq && key < Lk && (!CAUSAL || key <= q);
+  if constexpr (WIN)
+    v = v && (p.win_left < 0 || key >= q - p.win_left) && (p.win_right < 0 || key <= q + p.win_right);
+  return v;
+}
+
 // Index of the LSE / D value of token `tok` (sequence-local row i) of q-head
 // h: fixed length [B, Hq, Nq], packed [Hq, T].
 struct RowIndex {
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdParams p) {
 // dK, dV
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p, int n_kt) {
   using T = Tile<D>;
@@ -232,9 +242,16 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
   for (int t = 0; t < ND; ++t) dk[t] = dv[t] = f32x16{};
 
   // Query blocks: every q-head of the group, rows from the block that holds
-  // key k0 (causal) or from 0, to the end of the sequence.
-  const int qb0 = CAUSAL ? (k0 / kTileRows) * kTileRows : 0;
-  const int nqb = sb.Lq > qb0 ? (sb.Lq - qb0 + kTileRows - 1) / kTileRows : 0;
+  // key k0 (causal) or from 0, to the end of the sequence; with a window,
+  // only the rows whose windows reach keys k0 .. k0+127.
+  int qlo = CAUSAL ? k0 : 0;
+  int qhi = sb.Lq;
+  if constexpr (WIN) {
+    if (p.win_right >= 0) qlo = max(qlo, k0 - p.win_right);
+    if (p.win_left >= 0) qhi = min(qhi, k0 + kBwdRows - 1 + p.win_left + 1);
+  }
+  const int qb0 = (max(qlo, 0) / kTileRows) * kTileRows;
+  const int nqb = qhi > qb0 ? (qhi - qb0 + kTileRows - 1) / kTileRows : 0;
   const int n_it = nqb * gq;
   const float c = p.scale_log2;
 
@@ -273,6 +290,10 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
       const int qs0 = q0 + r0;  // its first query
       if (qs0 >= sb.Lq) break;
       if (CAUSAL && qs0 + 31 < kw0) continue;  // every query before every key of the wave
+      if constexpr (WIN) {  // every query outside every window of the wave's keys
+        if (p.win_right >= 0 && qs0 + 31 < kw0 - p.win_right) continue;
+        if (p.win_left >= 0 && qs0 > kw0 + 31 + p.win_left) continue;
+      }
       // S = Q K^T and dP = dO V^T: lane = key, register r = query qs0 + mrow(r)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -293,7 +314,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           const int q = qs0 + mrow(r, h2);
-          const bool vis = q < sb.Lq && key < sb.Lk && (!CAUSAL || key <= q);
+          const bool vis = visible<CAUSAL, WIN>(p, q, key, sb.Lq, sb.Lk);
           const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e] * kLog2e));
           pr[r] = vis ? pe : 0.f;
           dsr[r] = pr[r] * (dp[r] - dvv[e]);
@@ -338,7 +359,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
 // dQ
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdParams p, int n_qt) {
   using T = Tile<D>;
@@ -396,29 +417,40 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
 #pragma unroll
   for (int t = 0; t < ND; ++t) dq[t] = f32x16{};
 
+  // Key blocks: from 0 (or, with a window, the block holding the first
+  // row's window start) to the last key any row of the tile sees.
   int kend = sb.Lk;
   if (CAUSAL) kend = min(kend, min(q0 + kBwdRows, sb.Lq));
-  const int nkb = (kend + kTileRows - 1) / kTileRows;
+  int key_base = 0;
+  if constexpr (WIN) {
+    if (p.win_right >= 0) kend = min(kend, min(q0 + kBwdRows, sb.Lq) - 1 + p.win_right + 1);
+    if (p.win_left >= 0) key_base = (max(0, q0 - p.win_left) / kTileRows) * kTileRows;
+  }
+  const int nkb = kend > key_base ? (kend - key_base + kTileRows - 1) / kTileRows : 0;
   if (nkb > 0) {
-    issue_tile<D>(kg, kstride, 0, sb.Lk, k_st[0], tid, w);
-    issue_tile<D>(vg, kstride, 0, sb.Lk, v_st[0], tid, w);
+    issue_tile<D>(kg, kstride, key_base, sb.Lk, k_st[0], tid, w);
+    issue_tile<D>(vg, kstride, key_base, sb.Lk, v_st[0], tid, w);
   }
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 < nkb) {
-      issue_tile<D>(kg, kstride, (kb + 1) * kTileRows, sb.Lk, k_st[buf ^ 1], tid, w);
-      issue_tile<D>(vg, kstride, (kb + 1) * kTileRows, sb.Lk, v_st[buf ^ 1], tid, w);
+      issue_tile<D>(kg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, k_st[buf ^ 1], tid, w);
+      issue_tile<D>(vg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, v_st[buf ^ 1], tid, w);
     }
     const unsigned char* ks = k_st[buf];
     const unsigned char* vs = v_st[buf];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int r0 = 32 * sub;
-      const int ks0 = kb * kTileRows + r0;  // first key of this 32-key sub-block
+      const int ks0 = key_base + kb * kTileRows + r0;  // first key of this 32-key sub-block
       if (ks0 >= sb.Lk) break;
       if (CAUSAL && ks0 > wq0 + 31) break;  // every key after every query of the wave
+      if constexpr (WIN) {  // every key outside every window of the wave's rows
+        if (p.win_right >= 0 && ks0 > wq0 + 31 + p.win_right) break;
+        if (p.win_left >= 0 && ks0 + 31 < wq0 - p.win_left) continue;
+      }
       // S^T = K Q^T and dP^T = V dO^T: lane = query, register r = key ks0 + mrow(r)
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
@@ -430,7 +462,7 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = ks0 + mrow(r, h2);
-        const bool vis = qrow < sb.Lq && kk < sb.Lk && (!CAUSAL || kk <= qrow);
+        const bool vis = visible<CAUSAL, WIN>(p, qrow, kk, sb.Lq, sb.Lk);
         const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -lse2));
         dst[r] = vis ? pe * (dpt[r] - drow) : 0.f;
       }
@@ -467,8 +499,8 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
 // An empty side launches nothing for it: with Nq == 0 the dK/dV kernel
 // still runs and writes zeros (no query sees any key), with Nk == 0 the dQ
 // kernel writes zeros.
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+template <int D, bool CAUSAL, bool WIN>
+hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
   const long n_rows = static_cast<long>(p.batch) * p.nq * p.hq;
   if (n_rows > 0) {
     const long dot_blocks = (n_rows * (D / 8) + kThreads - 1) / kThreads;
@@ -477,7 +509,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qt = (p.nq + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN>),
                        dim3(static_cast<unsigned>(n_qt) * p.hq * p.batch), dim3(kThreads), 0,
                        stream, p, n_qt);
     const hipError_t e2 = hipGetLastError();
@@ -485,12 +517,18 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   }
   if (p.nk > 0) {
     const int n_kt = (p.nk + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN>),
                        dim3(static_cast<unsigned>(n_kt) * p.hkv * p.batch), dim3(kThreads), 0,
                        stream, p, n_kt);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  if (p.win_left >= 0 || p.win_right >= 0) return launch_bwd_main<D, CAUSAL, true>(p, stream);
+  return launch_bwd_main<D, CAUSAL, false>(p, stream);
 }
 
 #if !defined(FA_BF16_D) || !defined(FA_BF16_CAUSAL)

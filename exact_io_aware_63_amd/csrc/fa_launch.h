@@ -59,6 +59,8 @@ struct BwdParams {
   float scale;
   float scale_log2;           // scale * log2(e)
   int causal;
+  int win_left;               // sliding window as FwdParams (-1: unbounded)
+  int win_right;
 };
 
 // Launch the bf16 backward (D = rowsum(dO * O), then dQ, then dK and dV)

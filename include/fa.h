@@ -154,6 +154,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            float* Dsum, int B, int Hq, int Hkv, int Nq, int Nk, int d,
            float scale, int causal, const int32_t* cu_seqlens, void* stream);
 
+/* fa_bwd for the sliding-window forward of fa_fwd_window: the same window
+ * (LSE and O from fa_fwd_window with these window bounds). */
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O,
+                  const void* dO, const float* LSE, void* dQ, void* dK,
+                  void* dV, float* Dsum, int B, int Hq, int Hkv, int Nq,
+                  int Nk, int d, float scale, int causal, int window_left,
+                  int window_right, const int32_t* cu_seqlens, void* stream);
+
 /*
  * Split-K/V attention forward for decode-shaped problems, bf16: the same
  * function as fa_fwd (fixed-length layout, same mask and grouping) for few

@@ -26,7 +26,7 @@ def fa():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_fwd_splitkv",
+        ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_bwd_window", "fa_fwd_splitkv",
          "fa_fwd_splitkv_workspace_bytes",
          "fa_status_string", "fa_last_error", "fa_version"])
 

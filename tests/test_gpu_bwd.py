@@ -46,27 +46,29 @@ def _draw_do(shape, seed):
     return W.bf16_bits_to_f32(bits), bits
 
 
-def _run(inp, do_bits, causal, scale):
+def _run(inp, do_bits, causal, scale, window=None):
     """GPU forward then backward; returns float64 numpy (dq, dk, dv)."""
     import torch
 
     import exact_io_aware_63_amd as fa
     q, k, v, cu = to_device(inp)
     ms = inp.max_seqlen if cu is not None else None
-    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cu, max_seqlen=ms)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cu, max_seqlen=ms,
+                              window=window)
     do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(q.device)
     dq, dk, dv = fa.attention_bwd(q, k, v, o, lse, do, causal=causal, scale=scale, cu_seqlens=cu,
-                                  max_seqlen=ms)
+                                  max_seqlen=ms, window=window)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().double().numpy() for t in (dq, dk, dv))
 
 
-def _head_terms(qh, kh, vh, doh, scale, causal, rows=None):
+def _head_terms(qh, kh, vh, doh, scale, causal, rows=None, window=None):
     """P and dPa + Da (module docstring) of the given rows of one head
     (fp64; P from the definition, as the oracle forms it)."""
     lq, lk = qh.shape[0], kh.shape[0]
     rows = np.arange(lq) if rows is None else np.asarray(rows)
-    sc = np.where(oracle.visible_mask(rows, lk, causal), oracle.scores(qh[rows], kh, scale), -np.inf)
+    sc = np.where(oracle.visible_mask(rows, lk, causal, window), oracle.scores(qh[rows], kh, scale),
+                  -np.inf)
     p, _, _ = oracle.softmax_rows(sc)
     dpa = np.abs(doh[rows]) @ np.abs(vh).T
     da = (p * dpa).sum(axis=1, keepdims=True)
@@ -90,14 +92,14 @@ def _heads(inp, do):
                 yield s, h, g, q[s, :, h], k[s, :, g], v[s, :, g], do[s, :, h]
 
 
-def _bounds_full(inp, do, scale, causal):
+def _bounds_full(inp, do, scale, causal, window=None):
     """Elementwise magnitude sums of the module docstring, full tensors."""
     bq, bk, bv = (np.zeros(x.shape) for x in (inp.q, inp.k, inp.v))
     packed = inp.cu_seqlens is not None
     for s, h, g, qh, kh, vh, doh in _heads(inp, do):
         if qh.shape[0] == 0 or kh.shape[0] == 0:
             continue
-        p, w = _head_terms(qh, kh, vh, doh, scale, causal)
+        p, w = _head_terms(qh, kh, vh, doh, scale, causal, window=window)
         a = abs(scale) * ((p * w) @ np.abs(kh))
         b = abs(scale) * ((p * w).T @ np.abs(qh))
         c = p.T @ np.abs(doh)
@@ -160,6 +162,34 @@ def test_bwd_small_full_parity(case):
     got = _run(inp, do_bits, causal, scale)
     ref = oracle.attention_bwd_ref(inp.q, inp.k, inp.v, do, scale, causal, inp.cu_seqlens)
     bounds = _bounds_full(inp, do, scale, causal)
+    for nm, g, r, bd in zip(("dQ", "dK", "dV"), got, ref, bounds):
+        _check(f"{name} {nm}", g, r, bd)
+
+
+WINDOW_BWD = [
+    # B, Hq, Hkv, Nq, Nk, d, causal, lens, window
+    (2, 4, 2, 700, 700, 128, True, None, (100, -1)),
+    (1, 4, 4, 600, 600, 64, False, None, (64, 64)),
+    (1, 2, 1, 900, 900, 128, True, None, (257, 3)),
+    (1, 4, 1, 333, 200, 128, False, None, (-1, 30)),
+    (1, 4, 2, 0, 0, 128, True, [1, 127, 300, 0, 513, 64], (130, -1)),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_BWD,
+                         ids=[f"win{c[8][0]}_{c[8][1]}_" + _id(c[:8]) for c in WINDOW_BWD])
+def test_bwd_window_parity(case):
+    b, hq, hkv, nq, nk, d, causal, lens, win = case
+    name = f"win{win[0]}_{win[1]}_" + _id(case[:8])
+    say(f"[case] {name}")
+    seed = zlib.crc32(name.encode())
+    inp = W.draw(len(lens) if lens else b, hq, hkv, nq, nk, d, "bf16", seed=seed, lens=lens)
+    do, do_bits = _draw_do(inp.q.shape, seed + 1)
+    scale = 1.0 / math.sqrt(d)
+    got = _run(inp, do_bits, causal, scale, window=win)
+    ref = oracle.attention_bwd_ref(inp.q, inp.k, inp.v, do, scale, causal, inp.cu_seqlens,
+                                   window=win)
+    bounds = _bounds_full(inp, do, scale, causal, window=win)
     for nm, g, r, bd in zip(("dQ", "dK", "dV"), got, ref, bounds):
         _check(f"{name} {nm}", g, r, bd)
 
