@@ -4,11 +4,11 @@ infrastructure only).
 Only the tests, the smoke check and the bench's CPU-baseline leg use it; the
 product path never does.
 """
-from .attention import (ROW_CHUNK, attention_bwd_picked, attention_bwd_ref,
+from .attention import (ROW_CHUNK, attention_bwd_picked, attention_bwd_ref, bias_of,
                         attention_head, attention_head_bwd, attention_picked,
                         attention_ref, kv_head_of, scores, softmax_rows,
                         softmax_rows_bwd, visible_mask)
 
-__all__ = ["ROW_CHUNK", "attention_bwd_picked", "attention_bwd_ref", "attention_head",
+__all__ = ["ROW_CHUNK", "attention_bwd_picked", "attention_bwd_ref", "attention_head", "bias_of",
            "attention_head_bwd", "attention_picked", "attention_ref", "kv_head_of", "scores",
            "softmax_rows", "softmax_rows_bwd", "visible_mask"]

@@ -26,7 +26,14 @@ Readings taken where the pages are silent:
 * the retained row statistic is the natural-log log-sum-exp of the scaled,
   visible scores: LSE_i = m_i + log(sum_j exp(S_ij - m_i));
 * a row that sees no key has O = 0 and LSE = -inf;
-* no additive bias B, and V has the same width d as Q and K.
+* V has the same width d as Q and K;
+* the additive bias B of "Understanding FlashAttention Pt 1", section 0.2
+  (S = Q K^T / sqrt(d) + B) is optional. It is added to the scaled scores of
+  the visible pairs before the softmax; masked pairs stay masked whatever B
+  holds there, and a bias entry of -inf removes its pair like the mask does.
+  B is given per (batch entry or sequence, q-head) as a [Lq, Lk] block with
+  indices local to the sequence; ``bias_of`` states the indexing. The bias
+  is an input only: no gradient with respect to it is formed.
 
 The backward pass (``attention_head_bwd`` and the functions after it) is
 the gradient of the same function with respect to Q, K and V for a given
@@ -102,6 +109,25 @@ def visible_mask(rows: np.ndarray, lk: int, causal: bool, window=None) -> np.nda
     return m
 
 
+def bias_of(bias, s: int, h: int):
+    """The [Lq, Lk] bias block of batch entry (or sequence) ``s`` and q-head
+    ``h``, or None.
+
+    ``bias`` is None or an array indexed [s, h, i, j], i and j local to the
+    sequence; an axis of length 1 among the first two is shared by every
+    batch entry (or sequence) or every head. Reading: the pages define B
+    only as a term of S ("Understanding FlashAttention Pt 1", section 0.2),
+    so it is taken per (entry, head, query, key), the most general form, with
+    sharing as the usual broadcast.
+    """
+    if bias is None:
+        return None
+    b = np.asarray(bias)
+    if b.ndim != 4:
+        raise ValueError(f"bias must be indexed [s, h, i, j], got shape {b.shape}")
+    return b[s if b.shape[0] > 1 else 0, h if b.shape[1] > 1 else 0]
+
+
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     """S = scale * q_rows K^T, materialised ("Understanding FlashAttention
     Pt 1", section 0.2: S = Q K^T / sqrt(d); "Softmax does not need the
@@ -129,11 +155,13 @@ def softmax_rows(s: np.ndarray):
 
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   causal: bool, rows=None, window=None):
-    """One (sequence, head) of attention: q [Lq, d], k and v [Lk, d].
+                   causal: bool, rows=None, window=None, bias=None):
+    """One (sequence, head) of attention: q [Lq, d], k and v [Lk, d], bias
+    None or [>= Lq, >= Lk] (row i, column j: query i, key j).
 
-    Forms S, then P, then O = P V for the selected query rows (all rows if
-    ``rows`` is None), and LSE = m + log(l). Returns (O [R, d], LSE [R]).
+    Forms S (+ B), then P, then O = P V for the selected query rows (all
+    rows if ``rows`` is None), and LSE = m + log(l). Returns (O [R, d],
+    LSE [R]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -147,6 +175,8 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     for c0 in range(0, len(rows), ROW_CHUNK):
         r = rows[c0:c0 + ROW_CHUNK]
         s = scores(q[r], k, scale)                                # write S
+        if bias is not None:                                      # S + B
+            s = s + np.asarray(bias, dtype=np.float64)[r][:, :lk]
         s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, m, l = softmax_rows(s)                                 # write P
         out[c0:c0 + len(r)] = p @ v                               # O = P V
@@ -155,10 +185,14 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return out, lse
 
 
-def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None, window=None):
+def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None, window=None,
+                  bias=None):
     """Full forward pass in the token-major layouts of the module docstring.
 
-    Returns (O, LSE) as float64 arrays.
+    ``bias``: None or indexed [s, h, i, j] as ``bias_of`` states (fixed
+    length: [B or 1, Hq or 1, >= Nq, >= Nk]; packed: [nseq or 1, Hq or 1,
+    >= longest, >= longest], local indices). Returns (O, LSE) as float64
+    arrays.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -172,7 +206,7 @@ def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None, window=N
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
                 o_bh, l_bh = attention_head(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal,
-                                            window=window)
+                                            window=window, bias=bias_of(bias, b, h))
                 out[b, :, h] = o_bh
                 lse[b, h] = l_bh
         return out, lse
@@ -186,13 +220,14 @@ def attention_ref(q, k, v, scale: float, causal: bool, cu_seqlens=None, window=N
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             o_sh, l_sh = attention_head(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], scale, causal,
-                                        window=window)
+                                        window=window, bias=bias_of(bias, s, h))
             out[lo:hi, h] = o_sh
             lse[h, lo:hi] = l_sh
     return out, lse
 
 
-def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None, window=None):
+def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None, window=None,
+                     bias=None):
     """Selected outputs only, one (batch-or-sequence, q-head, row) at a time.
 
     For parity checks at sizes where the full oracle would take too long:
@@ -231,7 +266,7 @@ def attention_picked(q, k, v, scale: float, causal: bool, picks, cu_seqlens=None
                                       np.asarray(ks, dtype=np.float64),
                                       np.asarray(vs, dtype=np.float64),
                                       scale, causal, rows=picks[sel, 2],
-                                      window=window)
+                                      window=window, bias=bias_of(bias, int(s), int(h)))
         out[sel] = o_sel
         lse[sel] = l_sel
         i0 = i1
@@ -254,10 +289,11 @@ def softmax_rows_bwd(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
     return p * (dp - (p * dp).sum(axis=1, keepdims=True))
 
 
-def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None):
-    """Gradients of one (sequence, head): q, do [Lq, d]; k, v [Lk, d].
+def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None, bias=None):
+    """Gradients of one (sequence, head): q, do [Lq, d]; k, v [Lk, d]; bias
+    None or [>= Lq, >= Lk] as in ``attention_head``.
 
-    Forms S = scale q K^T, the mask, P = softmax_row(S) (as the forward
+    Forms S = scale q K^T (+ B), the mask, P = softmax_row(S) (as the forward
     definition), then
       dV = P^T dO,   dP = dO V^T,   dS = softmax_rows_bwd(P, dP),
       dQ = scale dS K,   dK = scale dS^T Q.
@@ -276,6 +312,8 @@ def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None):
     for c0 in range(0, lq, ROW_CHUNK):
         r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
         s = scores(q[r], k, scale)
+        if bias is not None:
+            s = s + np.asarray(bias, dtype=np.float64)[r][:, :lk]
         s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, _, _ = softmax_rows(s)
         dv += p.T @ do[r]
@@ -286,8 +324,10 @@ def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None):
     return dq, dk, dv
 
 
-def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, window=None):
-    """Gradients in the layouts of the module docstring (dO like O).
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, window=None,
+                      bias=None):
+    """Gradients in the layouts of the module docstring (dO like O); ``bias``
+    as in ``attention_ref``.
 
     Returns (dQ like q, dK like k, dV like v) as float64 arrays. With
     grouped-query attention a K/V head's gradients are the sums over the
@@ -307,7 +347,8 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, 
             for h in range(hq):
                 g = kv_head_of(h, hq, hkv)
                 a, bk, bv = attention_head_bwd(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h],
-                                               scale, causal, window=window)
+                                               scale, causal, window=window,
+                                               bias=bias_of(bias, b, h))
                 dq[b, :, h] = a
                 dk[b, :, g] += bk
                 dv[b, :, g] += bv
@@ -319,7 +360,8 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, 
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             a, bk, bv = attention_head_bwd(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], do[lo:hi, h],
-                                           scale, causal, window=window)
+                                           scale, causal, window=window,
+                                           bias=bias_of(bias, s, h))
             dq[lo:hi, h] = a
             dk[lo:hi, g] += bk
             dv[lo:hi, g] += bv
@@ -327,7 +369,7 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool, cu_seqlens=None, 
 
 
 def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_picks,
-                         cu_seqlens=None, window=None):
+                         cu_seqlens=None, window=None, bias=None):
     """Selected gradient rows, for parity checks at sizes where the full
     oracle would take too long.
 
@@ -351,6 +393,13 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
         hq, hkv = q.shape[1], k.shape[1]
         cu = np.asarray(cu_seqlens, dtype=np.int64)
 
+    def head_scores(qh, kh, s, h, r):
+        sc = scores(qh[r], kh, scale)
+        b = bias_of(bias, int(s), int(h))
+        if b is not None:
+            sc = sc + np.asarray(b, dtype=np.float64)[r][:, :kh.shape[0]]
+        return np.where(visible_mask(r, kh.shape[0], causal, window), sc, -np.inf)
+
     def head(s, h):
         g = kv_head_of(int(h), hq, hkv)
         if cu_seqlens is None:
@@ -364,9 +413,7 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
     for n, (s, h, i) in enumerate(q_picks):
         qh, kh, vh, doh = head(s, h)
         r = np.array([i])
-        sc = np.where(visible_mask(r, kh.shape[0], causal, window), scores(qh[r], kh, scale),
-                      -np.inf)
-        p, _, _ = softmax_rows(sc)
+        p, _, _ = softmax_rows(head_scores(qh, kh, s, h, r))
         ds = softmax_rows_bwd(p, doh[r] @ vh.T)
         dq[n] = scale * (ds @ kh)[0]
     dk = np.zeros((len(kv_picks), d))
@@ -382,9 +429,7 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
             lq, lk = qh.shape[0], kh.shape[0]
             for c0 in range(0, lq, ROW_CHUNK):
                 r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
-                sc = np.where(visible_mask(r, lk, causal, window), scores(qh[r], kh, scale),
-                              -np.inf)
-                p, _, _ = softmax_rows(sc)
+                p, _, _ = softmax_rows(head_scores(qh, kh, s, h, r))
                 ds = softmax_rows_bwd(p, doh[r] @ vh.T)
                 dv[sel] += p[:, cols].T @ doh[r]
                 dk[sel] += scale * (ds[:, cols].T @ qh[r])

@@ -292,9 +292,72 @@ def pin_bwd_window_finite_differences():
                           f"window directional {'QKV'[which]}")
 
 
+def pin_bwd_bias_finite_differences():
+    """Gradients with an additive bias (held fixed; causal and not, a bias
+    with -inf entries, GQA) against central differences of the biased
+    forward oracle."""
+    rng = _rng(113)
+    for causal, dead in ((True, False), (False, True)):
+        q = rng.standard_normal((1, 8, 2, 4))
+        k = rng.standard_normal((1, 9, 1, 4))
+        v = rng.standard_normal((1, 9, 1, 4))
+        do = rng.standard_normal((1, 8, 2, 4))
+        bias = rng.standard_normal((1, 2, 8, 9)) * 1.5
+        if dead:
+            bias[0, 0, :, 3] = -np.inf
+            bias[0, 1, 2, :] = -np.inf
+        dq, dk, dv = A.attention_bwd_ref(q, k, v, do, 0.6, causal, bias=bias)
+
+        def loss(qq, kk, vv):
+            return float((A.attention_ref(qq, kk, vv, 0.6, causal, bias=bias)[0] * do).sum())
+
+        for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            e = rng.standard_normal(x.shape)
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[which] = x + FD_EPS * e
+            args_m[which] = x - FD_EPS * e
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * FD_EPS)
+            _assert_close(float((g * e).sum()), fd, FD_TOL * max(1.0, abs(fd)),
+                          f"bias directional {'QKV'[which]}")
+
+
+def pin_bwd_bias_library_autograd():
+    """torch.autograd (CPU, float64) of softmax(scale Q K^T + B + mask) V
+    agrees with the oracle, for a bias per head and the causal mask."""
+    import torch
+    rng = _rng(114)
+    q = rng.standard_normal((2, 10, 2, 6))
+    k = rng.standard_normal((2, 10, 1, 6))
+    v = rng.standard_normal((2, 10, 1, 6))
+    do = rng.standard_normal((2, 10, 2, 6))
+    bias = rng.standard_normal((1, 2, 10, 10))
+    dq, dk, dv = A.attention_bwd_ref(q, k, v, do, 0.45, True, bias=bias)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kk = tk.repeat_interleave(2, dim=2)
+    vv = tv.repeat_interleave(2, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", tq, kk) * 0.45 + torch.tensor(bias)
+    s = s.masked_fill(~torch.ones(10, 10, dtype=torch.bool).tril(), float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), vv)
+    (o * torch.tensor(do)).sum().backward()
+    _assert_close(dq, tq.grad.numpy(), 1e-12, "autograd bias dQ")
+    _assert_close(dk, tk.grad.numpy(), 1e-12, "autograd bias dK")
+    _assert_close(dv, tv.grad.numpy(), 1e-12, "autograd bias dV")
+    qp = np.array([[0, 1, 9], [1, 0, 3]])
+    kp = np.array([[1, 0, 0], [0, 0, 7]])
+    pq, pk, pv = A.attention_bwd_picked(q, k, v, do, 0.45, True, qp, kp, bias=bias)
+    for r, (b, h, i) in enumerate(qp):
+        _assert_close(pq[r], dq[b, i, h], 1e-13, "picked bias dQ")
+    for r, (b, g, j) in enumerate(kp):
+        _assert_close(pk[r], dk[b, j, g], 1e-13, "picked bias dK")
+        _assert_close(pv[r], dv[b, j, g], 1e-13, "picked bias dV")
+
+
 ALL_BWD_PINS = [
     pin_bwd_finite_differences, pin_bwd_elementwise_numeric_gradient, pin_bwd_single_key,
     pin_bwd_zero_scale, pin_bwd_key_translation, pin_bwd_dv_column_sum,
     pin_bwd_gqa_is_repeated_heads, pin_bwd_packed_is_independent, pin_bwd_library_autograd,
     pin_bwd_picked_rows, pin_bwd_empty_and_zero_upstream, pin_bwd_window_finite_differences,
+    pin_bwd_bias_finite_differences, pin_bwd_bias_library_autograd,
 ]

@@ -496,11 +496,157 @@ def pin_window_brute_force():
         _assert_close(lse[i], m + math.log(den), 1e-13, "window brute-force LSE")
 
 
+def pin_bias_row_constant():
+    """A bias constant along each row (B_ij = c_i) cancels in the softmax:
+    O is unchanged and LSE_i moves by exactly c_i. Per (batch entry, head)
+    constants, causal and not, GQA, Nq != Nk."""
+    rng = _rng(41)
+    q = rng.standard_normal((2, 6, 3, 4))
+    k = rng.standard_normal((2, 8, 1, 4))
+    v = rng.standard_normal((2, 8, 1, 4))
+    c = rng.standard_normal((2, 3, 6))
+    bias = np.broadcast_to(c[..., None], (2, 3, 6, 8)).copy()
+    for causal in (False, True):
+        o, lse = A.attention_ref(q, k, v, 0.6, causal)
+        ob, lb = A.attention_ref(q, k, v, 0.6, causal, bias=bias)
+        _assert_close(ob, o, 1e-14, "row-constant bias O")
+        _assert_close(lb, lse + c, 1e-13, "row-constant bias LSE")
+
+
+def pin_bias_log_weights():
+    """With Q = 0 every score is 0, so B_ij = log w_j makes each row the
+    w-weighted mean of the visible values: O_i = sum w_j v_j / sum w_j and
+    LSE_i = log sum w_j (sums over j <= i when causal). A textbook weighted
+    mean; the bias is shared by all entries and heads ([1, 1, N, N])."""
+    rng = _rng(42)
+    n, d = 7, 3
+    w = rng.uniform(0.1, 3.0, n)
+    v = rng.standard_normal((1, n, 1, d))
+    q = np.zeros((1, n, 2, d))
+    k = rng.standard_normal((1, n, 1, d))
+    bias = np.broadcast_to(np.log(w)[None, None, None, :], (1, 1, n, n))
+    for causal in (False, True):
+        o, lse = A.attention_ref(q, k, v, 0.5, causal, bias=bias)
+        for i in range(n):
+            js = np.arange(i + 1 if causal else n)
+            want = (w[js, None] * v[0, js, 0]).sum(axis=0) / w[js].sum()
+            for h in range(2):
+                _assert_close(o[0, i, h], want, 1e-14, "log-weight bias O")
+                _assert_close(lse[0, h, i], np.log(w[js].sum()), 1e-14, "log-weight bias LSE")
+
+
+def pin_bias_as_mask():
+    """A bias of 0 and -inf is a mask: the lower-triangular pattern gives the
+    causal call, a band gives the windowed call, a row of -inf gives O = 0
+    and LSE = -inf, and -inf where the causal mask already hides changes
+    nothing."""
+    rng = _rng(43)
+    q = rng.standard_normal((1, 9, 2, 4))
+    k = rng.standard_normal((1, 9, 2, 4))
+    v = rng.standard_normal((1, 9, 2, 4))
+    i = np.arange(9)[:, None]
+    j = np.arange(9)[None, :]
+    tri = np.where(j <= i, 0.0, -np.inf)[None, None]
+    o, lse = A.attention_ref(q, k, v, 0.7, True)
+    ob, lb = A.attention_ref(q, k, v, 0.7, False, bias=tri)
+    _assert_close(ob, o, 0.0, "triangular bias O")
+    _assert_close(lb, lse, 0.0, "triangular bias LSE")
+    ob, lb = A.attention_ref(q, k, v, 0.7, True, bias=tri)
+    _assert_close(ob, o, 0.0, "triangular bias under causal O")
+    band = np.where((j >= i - 2) & (j <= i + 1), 0.0, -np.inf)[None, None]
+    o, lse = A.attention_ref(q, k, v, 0.7, False, window=(2, 1))
+    ob, lb = A.attention_ref(q, k, v, 0.7, False, bias=band)
+    _assert_close(ob, o, 0.0, "band bias O")
+    _assert_close(lb, lse, 0.0, "band bias LSE")
+    dead = np.zeros((1, 2, 9, 9))
+    dead[0, 1, 4, :] = -np.inf
+    ob, lb = A.attention_ref(q, k, v, 0.7, False, bias=dead)
+    assert np.all(ob[0, 4, 1] == 0) and np.isneginf(lb[0, 1, 4]), "fully masked row"
+    o, lse = A.attention_ref(q, k, v, 0.7, False)
+    keep = np.ones(o.shape, dtype=bool)
+    keep[0, 4, 1] = False
+    _assert_close(ob[keep], o[keep], 0.0, "other rows untouched")
+
+
+def pin_bias_brute_force():
+    """Pure-Python per-row evaluation of softmax(scale q.k_j + B_ij) with a
+    random bias (not square, causal)."""
+    rng = _rng(44)
+    lq, lk, d = 5, 7, 3
+    q = rng.standard_normal((lq, d))
+    k = rng.standard_normal((lk, d))
+    v = rng.standard_normal((lk, d))
+    b = rng.standard_normal((lq, lk)) * 2.0
+    o, lse = A.attention_head(q, k, v, 0.8, True, bias=b)
+    for i in range(lq):
+        keys = range(min(lk, i + 1))
+        s = [0.8 * math.fsum(q[i, c] * k[j, c] for c in range(d)) + b[i, j] for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        den = math.fsum(e)
+        for c in range(d):
+            _assert_close(o[i, c], math.fsum(e[n] * v[j, c] for n, j in enumerate(keys)) / den,
+                          1e-13, "bias brute-force O")
+        _assert_close(lse[i], m + math.log(den), 1e-13, "bias brute-force LSE")
+
+
+def pin_bias_library_sdpa():
+    """torch's scaled_dot_product_attention with an additive float mask
+    (CPU, float64) and torch.logsumexp agree with the oracle: a bias per
+    (entry, head), one shared over heads, and one combined with the causal
+    mask."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(45)
+    q = rng.standard_normal((2, 12, 4, 8))
+    k = rng.standard_normal((2, 12, 2, 8))
+    v = rng.standard_normal((2, 12, 2, 8))
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.repeat(k, 2, axis=2)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.repeat(v, 2, axis=2)).permute(0, 2, 1, 3)
+    tri = torch.zeros(12, 12, dtype=torch.float64).masked_fill(
+        ~torch.ones(12, 12, dtype=torch.bool).tril(), float("-inf"))
+    for shape, causal in (((2, 4, 12, 12), False), ((1, 4, 12, 12), True), ((2, 1, 12, 12), False)):
+        bias = rng.standard_normal(shape) * 1.5
+        o, lse = A.attention_ref(q, k, v, 0.35, causal, bias=bias)
+        mask = torch.from_numpy(bias) + (tri if causal else 0.0)
+        to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.35)
+        _assert_close(o, to.permute(0, 2, 1, 3).numpy(), ROUTE, "SDPA bias O")
+        sc = torch.matmul(tq, tk.transpose(-1, -2)) * 0.35 + mask
+        _assert_close(lse, torch.logsumexp(sc, dim=-1).numpy(), ROUTE, "logsumexp bias LSE")
+
+
+def pin_bias_packed():
+    """Packed sequences with a per-sequence bias block [nseq, Hq, Lmax, Lmax]
+    (local indices) equal separate fixed-length calls, each with its own
+    block cut to its length."""
+    rng = _rng(46)
+    cu = np.array([0, 5, 5, 12])
+    q = rng.standard_normal((12, 2, 4))
+    k = rng.standard_normal((12, 1, 4))
+    v = rng.standard_normal((12, 1, 4))
+    bias = rng.standard_normal((3, 2, 7, 7))
+    o, lse = A.attention_ref(q, k, v, 0.5, True, cu_seqlens=cu, bias=bias)
+    for s in range(3):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        n = hi - lo
+        os_, ls_ = A.attention_ref(q[None, lo:hi], k[None, lo:hi], v[None, lo:hi], 0.5, True,
+                                   bias=bias[s:s + 1, :, :n, :n])
+        _assert_close(o[lo:hi], os_[0], 0.0, "packed bias O")
+        _assert_close(lse[:, lo:hi], ls_[0], 0.0, "packed bias LSE")
+    picks = np.array([[0, 1, 4], [2, 0, 6], [2, 1, 0]])
+    po, pl = A.attention_picked(q, k, v, 0.5, True, picks, cu_seqlens=cu, bias=bias)
+    for r, (s, h, i) in enumerate(picks):
+        _assert_close(po[r], o[cu[s] + i, h], 1e-15, "picked bias O")
+        _assert_close(pl[r], lse[h, cu[s] + i], 1e-15, "picked bias LSE")
+
+
 ALL_PINS = [
     pin_rows_sum_to_one, pin_single_key, pin_uniform_scores_mean, pin_two_key_closed_form,
     pin_permutation_invariance, pin_brute_force, pin_online_route, pin_causal_structure,
     pin_gqa_is_repeated_heads, pin_packed_is_independent, pin_shift_invariance,
     pin_hard_max_limit, pin_library_sdpa, pin_empty_cases, pin_picked_rows,
     pin_window_wide_equals_plain, pin_window_zero_left_causal, pin_window_by_slicing,
-    pin_window_brute_force,
+    pin_window_brute_force, pin_bias_row_constant, pin_bias_log_weights, pin_bias_as_mask,
+    pin_bias_brute_force, pin_bias_library_sdpa, pin_bias_packed,
 ]

@@ -18,7 +18,7 @@ _orig_head_bwd = A.attention_head_bwd
 
 def _head_bwd_variant(change):
     """The oracle's per-head gradient steps with one planted change."""
-    def f(q, k, v, do, scale, causal, window=None):
+    def f(q, k, v, do, scale, causal, window=None, bias=None):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
         lq, lk = q.shape[0], k.shape[0]
         dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -26,6 +26,8 @@ def _head_bwd_variant(change):
             return dq, dk, dv
         r = np.arange(lq)
         s = A.scores(q, k, scale)
+        if bias is not None and change != "bias_ignored":
+            s = s + np.asarray(bias, dtype=np.float64)[:lq, :lk]
         if change != "mask_ignored":
             s = np.where(A.visible_mask(r, lk, causal, window), s, -np.inf)
         p, _, _ = A.softmax_rows(s)
@@ -40,7 +42,8 @@ def _head_bwd_variant(change):
     return f
 
 
-def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None, window=None):
+def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None, window=None,
+                              bias=None):
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     if cu_seqlens is None:
@@ -49,7 +52,7 @@ def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None, windo
             for h in range(hq):
                 g = A.kv_head_of(h, hq, hkv)
                 a, bk, bv = A.attention_head_bwd(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h],
-                                                 scale, causal)
+                                                 scale, causal, window, A.bias_of(bias, b, h))
                 dq[b, :, h], dk[b, :, g], dv[b, :, g] = a, bk, bv
         return dq, dk, dv
     hq, hkv = q.shape[1], k.shape[1]
@@ -59,7 +62,7 @@ def _bwd_ref_group_overwrites(q, k, v, do, scale, causal, cu_seqlens=None, windo
         for h in range(hq):
             g = A.kv_head_of(h, hq, hkv)
             a, bk, bv = A.attention_head_bwd(q[lo:hi, h], k[lo:hi, g], v[lo:hi, g], do[lo:hi, h],
-                                             scale, causal)
+                                             scale, causal, window, A.bias_of(bias, s, h))
             dq[lo:hi, h], dk[lo:hi, g], dv[lo:hi, g] = a, bk, bv
     return dq, dk, dv
 
@@ -77,6 +80,7 @@ MUTANTS = {
     "head_dv_from_ds": ("attention_head_bwd", _head_bwd_variant("dv_from_ds")),
     "head_dk_dv_swapped": ("attention_head_bwd", _head_bwd_variant("dk_dv_swapped")),
     "head_mask_ignored": ("attention_head_bwd", _head_bwd_variant("mask_ignored")),
+    "head_bias_ignored": ("attention_head_bwd", _head_bwd_variant("bias_ignored")),
     "gqa_group_overwrites": ("attention_bwd_ref", _bwd_ref_group_overwrites),
 }
 

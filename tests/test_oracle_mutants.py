@@ -75,7 +75,37 @@ def _window_right_off_by_one(rows, lk, causal, window=None):
     return m
 
 
+_orig_bias_of = A.bias_of
+
+
+def _head_with_bias(fn):
+    """attention_head with the bias block replaced by fn(bias, q)."""
+    def f(q, k, v, scale, causal, rows=None, window=None, bias=None):
+        return _orig_head(q, k, v, scale, causal, rows, window,
+                          None if bias is None else fn(np.asarray(bias, dtype=np.float64), scale))
+    return f
+
+
+def _head_bias_replaces_mask(q, k, v, scale, causal, rows=None, window=None, bias=None):
+    if bias is None:
+        return _orig_head(q, k, v, scale, causal, rows, window, bias)
+    return _orig_head(q, k, v, scale, False, rows, None, bias)
+
+
+def _bias_of_swapped(bias, s, h):
+    if bias is None:
+        return None
+    b = np.asarray(bias)
+    return b[h if b.shape[0] > 1 else 0, s if b.shape[1] > 1 else 0]
+
+
 MUTANTS = {
+    "bias_ignored": ("attention_head", _head_with_bias(lambda b, scale: np.zeros_like(b))),
+    "bias_transposed": ("attention_head", _head_with_bias(lambda b, scale: b.T)),
+    "bias_negated": ("attention_head", _head_with_bias(lambda b, scale: -b)),
+    "bias_scaled": ("attention_head", _head_with_bias(lambda b, scale: b * scale)),
+    "bias_replaces_mask": ("attention_head", _head_bias_replaces_mask),
+    "bias_entry_head_swapped": ("bias_of", _bias_of_swapped),
     "window_ignored": ("visible_mask", lambda rows, lk, causal, window=None:
                        _orig_visible(rows, lk, causal, None)),
     "window_left_off_by_one": ("visible_mask", _window_left_off_by_one),
@@ -90,19 +120,19 @@ MUTANTS = {
     "softmax_wrong_axis": ("softmax_rows", _softmax_wrong_axis),
     "lse_without_denominator": ("softmax_rows", _softmax_lse_no_l),
     "values_are_keys": ("attention_head",
-                        lambda q, k, v, scale, causal, rows=None, window=None:
-                        _orig_head(q, k, k, scale, causal, rows, window)),
+                        lambda q, k, v, scale, causal, rows=None, window=None, bias=None:
+                        _orig_head(q, k, k, scale, causal, rows, window, bias)),
     "lse_log2": ("attention_head",
-                 lambda q, k, v, scale, causal, rows=None, window=None:
+                 lambda q, k, v, scale, causal, rows=None, window=None, bias=None:
                  (lambda o, l: (o, l / np.log(2.0)))(*_orig_head(q, k, v, scale, causal, rows,
-                                                                 window))),
+                                                                 window, bias))),
     "last_key_dropped": ("attention_head",
-                         lambda q, k, v, scale, causal, rows=None, window=None:
-                         _orig_head(q, k[:-1], v[:-1], scale, causal, rows, window)),
+                         lambda q, k, v, scale, causal, rows=None, window=None, bias=None:
+                         _orig_head(q, k[:-1], v[:-1], scale, causal, rows, window, bias)),
     "first_row_skipped": ("attention_head",
-                          lambda q, k, v, scale, causal, rows=None, window=None:
+                          lambda q, k, v, scale, causal, rows=None, window=None, bias=None:
                           (lambda o, l: (np.concatenate([np.zeros_like(o[:1]), o[1:]]), l))(
-                              *_orig_head(q, k, v, scale, causal, rows, window))),
+                              *_orig_head(q, k, v, scale, causal, rows, window, bias))),
 }
 
 
