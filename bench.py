@@ -23,6 +23,8 @@ on the same workload instead: 10*d algorithmic flops per visible pair
 times ``fa_fwd_splitkv`` on a decode shape built from the workload's heads
 (``--decode-batch`` sequences, each with N cached keys and one new query
 that sees them all): HBM-bound, reported in GB/s of algorithmic bytes.
+``--window LEFT`` times ``fa_fwd_window`` and ``--bias shared|per-head``
+``fa_fwd_bias`` (flops of the visible pairs; the bias bytes are reported).
 """
 from __future__ import annotations
 
@@ -144,11 +146,12 @@ def recorded_traffic():
 # CPU baseline: the oracle on a bounded sample of the workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(inp, w, budget_s: float = 12.0, do=None):
+def cpu_baseline(inp, w, budget_s: float = 12.0, do=None, bias_block=None):
     """Time the fp64 oracle on whole (sequence, head) units of the workload
     until about ``budget_s`` seconds of CPU work, and scale to TFLOP/s with
     the same algorithmic flop count as the GPU figure. With ``do`` (the
-    upstream gradient) the oracle's backward pass is timed instead."""
+    upstream gradient) the oracle's backward pass is timed instead; with
+    ``bias_block`` (s, h) -> [Lq, >= Lk] array the biased forward."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -174,7 +177,8 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None):
             qs, ks, vs = inp.q[lo:hi, h], inp.k[lo:hi, g], inp.v[lo:hi, g]
             dos = do[lo:hi, h] if do is not None else None
         if do is None:
-            oracle.attention_head(qs, ks, vs, w.scale, w.causal)
+            bb = bias_block(s, h) if bias_block is not None else None
+            oracle.attention_head(qs, ks, vs, w.scale, w.causal, bias=bb)
         else:
             oracle.attention_head_bwd(qs, ks, vs, dos, w.scale, w.causal)
         flops += (4 if do is None else 10) * w.d * visible_pairs(lens_q[s], lens_k[s], w.causal)
@@ -189,7 +193,8 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None):
         "kind": "oracle",
         "sample": (f"{done} of {len(units)} (sequence, q-head) units of the same workload, "
                    f"full rows, fp64 numpy materialising S and P"
-                   f"{' (gradients)' if do is not None else ''}; {dt:.1f} s wall; "
+                   f"{' (gradients)' if do is not None else ''}"
+                   f"{' (with the bias)' if bias_block is not None else ''}; {dt:.1f} s wall; "
                    f"BLAS threads {threads}, host cpus {len(os.sched_getaffinity(0))}"),
     }
 
@@ -313,6 +318,10 @@ def main(argv=None):
     ap.add_argument("--window", type=int, default=-1, metavar="LEFT",
                     help="forward with a sliding window of LEFT keys before each query "
                          "(fa_fwd_window; bf16)")
+    ap.add_argument("--bias", choices=("none", "shared", "per-head"), default="none",
+                    help="forward with an additive bf16 bias (fa_fwd_bias): one [N, N] bias "
+                         "shared by every head, or one per (entry, head); N(0, 1) values drawn "
+                         "on the device from a seeded generator")
     ap.add_argument("--decode-batch", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -406,6 +415,26 @@ def main(argv=None):
                                   int(w.causal), args.window, -1, cu_ptr, sptr)
             if st != 0:
                 raise RuntimeError(f"fa_fwd_window failed: {fa.fa_last_error()}")
+    bias_t = None
+    if args.bias != "none" and args.which == "fwd":
+        if w.dtype != "bf16" or w.packed or args.window >= 0:
+            print("--bias needs a fixed-length bf16 workload and no window", file=sys.stderr)
+            return 2
+        npad = (Nk + 3) // 4 * 4
+        shape = (1, 1, Nq, npad) if args.bias == "shared" else (B, w.hq, Nq, npad)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(3000 + w.wid)
+        bias_t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(
+            torch.bfloat16)
+        sb, sh, sr = fa.bias_strides(bias_t, B, w.hq, Nq, Nk)
+
+        def fwd_step():  # noqa: F811  (the biased forward replaces the plain one)
+            st = fa.fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d, w.scale,
+                                int(w.causal), bias_t.data_ptr(), sb, sh, sr, cu_ptr, sptr)
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_bias failed: {fa.fa_last_error()}")
+        torch.cuda.synchronize()
     step = fwd_step
     do_np = None
     if args.which == "bwd":
@@ -476,7 +505,7 @@ def main(argv=None):
     win = (args.window, -1) if (args.window >= 0 and args.which == "fwd") else None
     flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal,
                               per_pair=10 if args.which == "bwd" else 4, window=win)
-    if win is not None:
+    if win is not None or bias_t is not None:
         headline = False
     tq, tk = sum(lens_q), sum(lens_k)
     abytes = (algorithmic_bytes_bwd if args.which == "bwd" else algorithmic_bytes)(
@@ -496,7 +525,8 @@ def main(argv=None):
     line = {
         "metric": (METRIC if (headline and args.which == "fwd")
                    else f"attention {args.which} TFLOP/s ({w.name}"
-                        f"{f', window {args.window}' if win is not None else ''})"),
+                        f"{f', window {args.window}' if win is not None else ''}"
+                        f"{f', {args.bias} bias' if bias_t is not None else ''})"),
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -522,6 +552,10 @@ def main(argv=None):
         "detail": {
             "alg_flops": flops,
             "alg_hbm_bytes": abytes,
+            "bias": ({"kind": args.bias, "shape": list(bias_t.shape),
+                      "visible_bias_bytes": 2 * visible_pairs(Nq, Nk, w.causal) * (
+                          1 if args.bias == "shared" else B * w.hq)}
+                     if bias_t is not None else None),
             "standard_path_bytes_avoided": standard_path_bytes_avoided(lens_q, w.hq),
             "launch_ms": {"mean": avg_launch_ms, "min": float(np.min(per_launch_ms)),
                           "median": float(np.median(per_launch_ms)),
@@ -537,7 +571,13 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget, do=do_np)
+        bias_block = None
+        if bias_t is not None:
+            def bias_block(s, h):
+                return bias_t[0 if bias_t.shape[0] == 1 else s,
+                              0 if bias_t.shape[1] == 1 else h].float().cpu().double().numpy()
+        line["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget, do=do_np,
+                                            bias_block=bias_block)
     print(json.dumps(line), flush=True)
     return 0 if ok else 3
 

@@ -4,7 +4,8 @@ Argument marshalling only: every step of the attention forward runs in the
 HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
-The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_bwd``, ``fa_status_string``,
+The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_fwd_window``, ``fa_fwd_bias``,
+``fa_bwd``, ``fa_bwd_window``, ``fa_fwd_splitkv``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
 wrapper that checks torch tensors, allocates O and LSE with torch and calls
@@ -49,6 +50,10 @@ _lib.fa_fwd_window.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
                                [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_fwd_window.restype = ctypes.c_int
+_lib.fa_fwd_bias.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                             [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p])
+_lib.fa_fwd_bias.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_bwd.restype = ctypes.c_int
@@ -69,8 +74,9 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_bwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
-            "fa_status_string", "fa_last_error", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
+            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_status_string",
+            "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -97,6 +103,33 @@ def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window_
     """C ``fa_fwd_window``: pointers are integer device addresses (or 0 / None)."""
     return _lib.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
                               window_left, window_right, cu_seqlens, stream)
+
+
+def fa_fwd_bias(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, bias, bias_stride_b,
+                bias_stride_h, bias_stride_row, cu_seqlens, stream) -> int:
+    """C ``fa_fwd_bias``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd_bias(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal), bias,
+                            bias_stride_b, bias_stride_h, bias_stride_row, cu_seqlens, stream)
+
+
+def bias_strides(bias, n_entries, hq, nq, nk):
+    """Element strides (entry, head, row) of a bf16 bias tensor indexed
+    [entry or 1, Hq or 1, >= Nq, >= Nk] with contiguous rows; an axis of
+    extent 1 gets stride 0 (shared)."""
+    import torch
+
+    if bias.dtype != torch.bfloat16 or not bias.is_cuda or bias.dim() != 4:
+        raise ValueError("bias must be a 4-D bfloat16 device tensor [entries|1, Hq|1, rows, cols]")
+    if bias.shape[0] not in (1, n_entries) or bias.shape[1] not in (1, hq):
+        raise ValueError(f"bias shape {tuple(bias.shape)} does not match {n_entries} entries "
+                         f"and {hq} heads")
+    if bias.shape[2] < nq or bias.shape[3] < nk:
+        raise ValueError(f"bias shape {tuple(bias.shape)} does not cover Nq={nq}, Nk={nk}")
+    if bias.stride(3) != 1 and bias.shape[3] > 1:
+        raise ValueError("bias rows must be contiguous")
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    sh = 0 if bias.shape[1] == 1 else bias.stride(1)
+    return sb, sh, bias.stride(2)
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
@@ -131,14 +164,16 @@ def fa_version() -> int:
 
 
 def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
-                  max_seqlen=None, out=None, lse=None, stream=None, window=None):
+                  max_seqlen=None, out=None, lse=None, stream=None, window=None, bias=None):
     """Attention forward on torch device tensors through the C ABI.
 
     Fixed length: q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d].
     Packed: q [T, Hq, d], k and v [T, Hkv, d], ``cu_seqlens`` int32 [nseq+1]
     on the device and ``max_seqlen`` the longest sequence (a host int).
     bf16 tensors go to ``fa_fwd``, float32 tensors to ``fa_fwd_fp32``;
-    ``window`` = (left, right) selects ``fa_fwd_window`` (bf16 only).
+    ``window`` = (left, right) selects ``fa_fwd_window`` (bf16 only);
+    ``bias`` (bf16 [B or 1, Hq or 1, >= Nq, >= Nk], packed: per sequence,
+    local indices) selects ``fa_fwd_bias``.
     Returns (O, LSE); O has q's shape and dtype, LSE is float32 [B, Hq, Nq]
     (packed: [Hq, T]).
     """
@@ -189,7 +224,16 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
         lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if window is not None:
+    if bias is not None:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("a bias needs bfloat16 tensors")
+        if window is not None:
+            raise ValueError("a window and a bias do not combine; write the window into the bias")
+        sb, sh, sr = bias_strides(bias, B, Hq, Nq, Nk)
+        st = _lib.fa_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                              int(bool(causal)), bias.data_ptr(), sb, sh, sr, cu_ptr, stream)
+    elif window is not None:
         if q.dtype != torch.bfloat16:
             raise TypeError("a sliding window needs bfloat16 tensors")
         st = _lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -105,14 +105,35 @@ int validate(const void* Q, const void* K, const void* V, const void* O, const f
   return FA_OK;
 }
 
+// Additive bias of fa_fwd_bias: bf16 element (s, h, i, j) at
+// ptr[s*sb + h*sh + i*sr + j].
+struct BiasArg {
+  const void* ptr;
+  int64_t sb, sh, sr;
+};
+
+int validate_bias(const BiasArg& b, int Nk) {
+  if (b.ptr == nullptr) return fail(FA_ERR_NULL, "bias must be non-NULL");
+  if (!aligned(b.ptr, 8)) return fail(FA_ERR_ARG, "bias must be 8-byte aligned");
+  if (b.sb < 0 || b.sh < 0)
+    return fail(FA_ERR_ARG, "bias strides of the batch and head axes must be >= 0 (0 shares)");
+  if (b.sr < Nk)
+    return fail(FA_ERR_ARG, "bias row stride %lld is smaller than Nk=%d",
+                static_cast<long long>(b.sr), Nk);
+  if (b.sb % 4 != 0 || b.sh % 4 != 0 || b.sr % 4 != 0)
+    return fail(FA_ERR_ARG, "bias strides must be multiples of 4 elements");
+  return FA_OK;
+}
+
 int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
         int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
-        void* stream, int win_left = -1, int win_right = -1) {
+        void* stream, int win_left = -1, int win_right = -1, const BiasArg* bias = nullptr) {
   g_last_error[0] = '\0';
   bool noop = false;
   const int tile_rows = bf16 ? fa::kBf16TileRows : fa::kFp32TileRows;
   int st = validate(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, cu_seqlens, tile_rows, &noop);
   if (st != FA_OK || noop) return st;
+  if (bias != nullptr && (st = validate_bias(*bias, Nk)) != FA_OK) return st;
   st = check_device();
   if (st != FA_OK) return st;
   fa::FwdParams p;
@@ -132,6 +153,11 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   p.causal = causal ? 1 : 0;
   p.win_left = win_left < 0 ? -1 : win_left;
   p.win_right = win_right < 0 ? -1 : win_right;
+  p.scale = scale;
+  p.bias = bias ? bias->ptr : nullptr;
+  p.bias_sb = bias ? bias->sb : 0;
+  p.bias_sh = bias ? bias->sh : 0;
+  p.bias_sr = bias ? bias->sr : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (!bf16)
@@ -312,6 +338,15 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
                   int window_right, const int32_t* cu_seqlens, void* stream) {
   return run(true, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream,
              window_left, window_right);
+}
+
+int fa_fwd_bias(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+                int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* bias,
+                int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_row,
+                const int32_t* cu_seqlens, void* stream) {
+  const BiasArg b{bias, bias_stride_b, bias_stride_h, bias_stride_row};
+  return run(true, Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, cu_seqlens, stream, -1,
+             -1, &b);
 }
 
 int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O, float* LSE, int B,

@@ -164,7 +164,13 @@ static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
 // (a negative bound is unbounded), on top of the causal mask. The
 // workgroup streams only the key blocks its rows' windows reach; blocks
 // are indexed from the first of them, kb_base.
-template <int D, bool CAUSAL, bool WIN>
+// BIAS: an additive bf16 bias B joins the scores of the visible pairs
+// before the softmax ("Understanding FlashAttention Pt 1", section 0.2:
+// S = Q K^T / sqrt(d) + B). Each lane loads the bias values of its own
+// score registers (runs of 4 consecutive keys, 8 bytes) straight into
+// registers, one block ahead; scores then carry t = scale * s + b in
+// natural units and the base-2 factor becomes log2(e).
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdParams p, int n_qt) {
   using T = Tile<D>;
@@ -266,9 +272,49 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   }
 
   // A negative scale is applied by negating Q (exact in bf16), so that the
-  // base-2 factor c below is >= 0 and max(c*s) = c*max(s).
+  // base-2 factor c below is >= 0 and max(c*s) = c*max(s). With a bias the
+  // scores become t = cn * s + b first and the base-2 factor is log2(e).
   const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
+  const float cn = fmaxf(fabsf(p.scale), FLT_MIN);
+  const float ce = BIAS ? 1.4426950408889634f : c;
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+
+  // Bias rows of this lane, one per query tile (rows past the end read the
+  // last row; they are never stored), and the bias values of one block:
+  // bb[qt][kt][g] holds keys k0 + 32kt + 8g + 4*h2 + (0..3), i.e. score
+  // registers 4g .. 4g+3 of sc[qt][kt]. A run never crosses the end of a
+  // row: the row stride is a multiple of 4 and at least Nk, and in a block
+  // that reaches past the keys every run start is clamped to the last run.
+  const u16* brow[2] = {nullptr, nullptr};
+  u32x2 bb[2][2][4];
+  if constexpr (BIAS) {
+    const u16* bg = static_cast<const u16*>(p.bias) + b * p.bias_sb + h * p.bias_sh;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      brow[qt] = bg + static_cast<long>(min(wq0 + 32 * qt + j, Lq - 1)) * p.bias_sr + 4 * h2;
+  }
+  auto load_bias = [&](int jb) {
+    const int k0 = key_base + jb * kBC;
+    if (k0 + kBC <= Lk) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bb[qt][kt][g] = *reinterpret_cast<const u32x2*>(brow[qt] + k0 + 32 * kt + 8 * g);
+    } else {
+      const int kmax = ((Lk - 1) & ~3) - 4 * h2;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bb[qt][kt][g] =
+                *reinterpret_cast<const u32x2*>(brow[qt] + min(k0 + 32 * kt + 8 * g, kmax));
+    }
+  };
 
   // Q fragments, held in registers for the whole key loop: the B operand of
   // S^T = K Q^T (column = query, 8 consecutive d values per lane). Query
@@ -287,6 +333,9 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     }
   }
   asm volatile("s_nop 4" ::: "memory");     // AGPR writes before MFMA reads
+  if constexpr (BIAS) {
+    if (nblk_w > 0) load_bias(0);
+  }
 
   f32x16 acc[2][ND];
 #pragma unroll
@@ -430,6 +479,21 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         }
       }
     }
+    if constexpr (BIAS) {  // t = cn * s + b; masked scores stay -inf
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wd = bb[qt][kt][g][e >> 1];
+              const float bv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+              sc[qt][kt][4 * g + e] = __builtin_fmaf(sc[qt][kt][4 * g + e], cn, bv);
+            }
+      if (jb + 1 < nblk_w) load_bias(jb + 1);
+    }
     float mb[2];
     bool up = false;
 #pragma unroll
@@ -439,7 +503,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[qt][0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qt][1][r]);
-      mb[qt] = xhalf_max(mx) * c;
+      mb[qt] = xhalf_max(mx) * ce;
       // A row's first visible block sets its reference (its accumulator and
       // denominator are still zero); later raises need the rescale.
       if (m_run[qt] == -INFINITY) m_run[qt] = mb[qt];
@@ -494,7 +558,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         if constexpr (E < 64) {
           constexpr int eg = E / 16, eq = (E / 8) & 1, es = E % 8;
           const float x = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[eq][eg >> 1][8 * (eg & 1) + es], c, -m_ref[eq]));
+              __builtin_fmaf(sc[eq][eg >> 1][8 * (eg & 1) + es], ce, -m_ref[eq]));
           rs[eq][eg] += x;
           pb[eq][eg][es] = static_cast<__bf16>(x);
         }
@@ -556,12 +620,15 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int n_qt = (p.nq + kBR - 1) / kBR;
   const unsigned grid = static_cast<unsigned>(n_qt) * p.hq * p.batch;
-  if (p.win_left >= 0 || p.win_right >= 0)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(grid), dim3(kThreads), 0, stream,
-                       p, n_qt);
+  if (p.bias != nullptr)  // the host never combines a bias with a window
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, p, n_qt);
+  else if (p.win_left >= 0 || p.win_right >= 0)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, p, n_qt);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(kThreads), 0, stream,
-                       p, n_qt);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, p, n_qt);
   return hipGetLastError();
 }
 

@@ -25,6 +25,11 @@ struct FwdParams {
   int causal;
   int win_left;               // sliding window: query i sees keys >= i - win_left (-1: all)
   int win_right;              // and keys <= i + win_right (-1: all); bf16 kernels only
+  float scale;                // the score scale itself (bias variant)
+  const void* bias;           // additive bias, bf16, or nullptr; bf16 kernels only:
+  long bias_sb;               //   element (s, h, i, j) at bias[s*sb + h*sh + i*sr + j]
+  long bias_sh;
+  long bias_sr;
 };
 
 // Launch the bf16 kernel for head width D (64 or 128), causal or not.

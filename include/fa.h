@@ -115,6 +115,36 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O,
                   float scale, int causal, int window_left, int window_right,
                   const int32_t* cu_seqlens, void* stream);
 
+/*
+ * fa_fwd with an additive bias B in the scores: S = scale * Q K^T + B,
+ * P = softmax_row(S) over the visible keys ("Understanding FlashAttention
+ * Pt 1: Personal Notes", section 0.2 Notation, where B is an optional
+ * additive mask or bias).
+ *   bias : device pointer, bf16, 8-byte aligned. Element (s, h, i, j), for
+ *          batch entry (or packed sequence) s, query head h, query i and
+ *          key j (i, j local to the entry or sequence), is
+ *          bias[s*bias_stride_b + h*bias_stride_h + i*bias_stride_row + j].
+ *   bias_stride_b, bias_stride_h : >= 0, in elements; 0 shares one bias
+ *          over every entry or every head.
+ *   bias_stride_row : in elements, >= Nk.
+ *   All three strides must be multiples of 4. Bias rows are read in aligned
+ *   runs of 4 elements, so positions up to the next multiple of 4 past a
+ *   row's last key must be readable (values read past the last key are
+ *   ignored); a row stride that is a multiple of 4 and >= Nk guarantees
+ *   this inside a row.
+ * The causal mask still applies (a masked pair stays masked whatever B
+ * holds). B may hold -inf, which removes a pair; a row left with no visible
+ * pair gets O = 0 and LSE = -inf. +inf or NaN in B give undefined results.
+ * LSE is the log-sum-exp of the biased scores. No sliding window with a
+ * bias (a window is a bias of 0 and -inf). No gradient with respect to B.
+ * Other arguments and errors as fa_fwd.
+ */
+int fa_fwd_bias(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                int causal, const void* bias, int64_t bias_stride_b,
+                int64_t bias_stride_h, int64_t bias_stride_row,
+                const int32_t* cu_seqlens, void* stream);
+
 /* Same contract with float32 Q, K, V, O (no bf16 rounding anywhere). */
 int fa_fwd_fp32(const float* Q, const float* K, const float* V, float* O,
                 float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,

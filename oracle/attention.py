@@ -176,7 +176,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         r = rows[c0:c0 + ROW_CHUNK]
         s = scores(q[r], k, scale)                                # write S
         if bias is not None:                                      # S + B
-            s = s + np.asarray(bias, dtype=np.float64)[r][:, :lk]
+            s = s + np.asarray(np.asarray(bias)[r][:, :lk], dtype=np.float64)
         s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, m, l = softmax_rows(s)                                 # write P
         out[c0:c0 + len(r)] = p @ v                               # O = P V
@@ -313,7 +313,7 @@ def attention_head_bwd(q, k, v, do, scale: float, causal: bool, window=None, bia
         r = np.arange(c0, min(lq, c0 + ROW_CHUNK))
         s = scores(q[r], k, scale)
         if bias is not None:
-            s = s + np.asarray(bias, dtype=np.float64)[r][:, :lk]
+            s = s + np.asarray(np.asarray(bias)[r][:, :lk], dtype=np.float64)
         s = np.where(visible_mask(r, lk, causal, window), s, -np.inf)
         p, _, _ = softmax_rows(s)
         dv += p.T @ do[r]
@@ -397,7 +397,7 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
         sc = scores(qh[r], kh, scale)
         b = bias_of(bias, int(s), int(h))
         if b is not None:
-            sc = sc + np.asarray(b, dtype=np.float64)[r][:, :kh.shape[0]]
+            sc = sc + np.asarray(np.asarray(b)[r][:, :kh.shape[0]], dtype=np.float64)
         return np.where(visible_mask(r, kh.shape[0], causal, window), sc, -np.inf)
 
     def head(s, h):

@@ -26,7 +26,8 @@ def fa():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_bwd", "fa_bwd_window", "fa_fwd_splitkv",
+        ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
+         "fa_fwd_splitkv",
          "fa_fwd_splitkv_workspace_bytes",
          "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -114,6 +115,48 @@ def test_valid_call_without_gpu_fails_cleanly(fa):
     st = _call(fa, fa.fa_fwd)
     assert st == fa.FA_ERR_HIP
     assert "hip" in fa.fa_last_error().lower()
+
+
+def _call_bias(fa, bias=P, sb=0, sh=64, sr=8, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd_bias(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], bias, sb, sh, sr,
+                          a["cu"], a["stream"])
+
+
+BAD_BIAS = [
+    ("null_bias", dict(bias=0), -1),
+    ("misaligned_bias", dict(bias=P + 4), -4),
+    ("negative_entry_stride", dict(sb=-4), -4),
+    ("negative_head_stride", dict(sh=-64), -4),
+    ("row_stride_below_nk", dict(sr=4), -4),
+    ("row_stride_not_multiple_of_4", dict(sr=10), -4),
+    ("head_stride_not_multiple_of_4", dict(sh=66), -4),
+    ("entry_stride_not_multiple_of_4", dict(sb=2), -4),
+    ("base_checks_still_apply", dict(Hq=6, Hkv=4), -2),
+    ("null_q", dict(q=0), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_BIAS, ids=[b[0] for b in BAD_BIAS])
+def test_bias_rejects_bad_arguments(fa, name, kw, status):
+    st = _call_bias(fa, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error()
+
+
+def test_bias_empty_work_is_a_noop(fa):
+    assert _call_bias(fa, B=0, bias=0) == 0
+    assert _call_bias(fa, Nq=0) == 0
+
+
+def test_bias_valid_call_without_gpu_fails_cleanly(fa):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_bias(fa) == fa.FA_ERR_HIP
+    assert _call_bias(fa, sb=0, sh=0, sr=8, causal=1) == fa.FA_ERR_HIP
 
 
 def test_attention_fwd_checks_tensors(fa):

@@ -146,3 +146,48 @@ def draw_workload(wid: int, seed: Optional[int] = None) -> Inputs:
         return draw(w.batch, w.hq, w.hkv, 0, 0, w.d, w.dtype, seed, sig,
                     lens=("uniform", lo, hi))
     return draw(w.batch, w.hq, w.hkv, w.n, w.n, w.d, w.dtype, seed, sig)
+
+
+@dataclasses.dataclass
+class Bias:
+    """An additive bias as bf16 bit patterns and the float32 values they
+    hold, indexed [entry or 1, head or 1, row, column]; the columns are
+    padded with zeros to a multiple of 4 (the row stride the bf16 kernels
+    read in runs of 4)."""
+    values: np.ndarray
+    bits: np.ndarray
+
+
+def draw_bias(entries: int, heads: int, rows: int, cols: int, seed: int, sigma: float = 1.0,
+              key_lens=None, dead_rows=()) -> Bias:
+    """Draw a bias [entries, heads, rows, round_up(cols, 4)].
+
+    Entries are ``rng.standard_normal(float32) * sigma`` from
+    ``numpy.random.default_rng(seed)``, rounded to bf16. ``key_lens`` (one
+    length per entry) sets columns at or past that length to -inf, a key
+    padding pattern; ``dead_rows`` lists (entry, head, row) triples whose
+    whole row is -inf. Padding columns past ``cols`` hold 0.
+    """
+    rng = np.random.default_rng(seed)
+    cpad = (cols + 3) // 4 * 4
+    x = np.zeros((entries, heads, rows, cpad), dtype=np.float32)
+    x[..., :cols] = rng.standard_normal((entries, heads, rows, cols), dtype=np.float32) * np.float32(
+        sigma)
+    if key_lens is not None:
+        for e, n in enumerate(key_lens):
+            x[e, :, :, int(n):cols] = -np.inf
+    for e, h, r in dead_rows:
+        x[e, h, r, :cols] = -np.inf
+    bits = round_to_bf16_bits_inf(x)
+    return Bias(bf16_bits_to_f32(bits), bits)
+
+
+def round_to_bf16_bits_inf(x: np.ndarray) -> np.ndarray:
+    """``round_to_bf16_bits`` that also keeps infinities (their bit patterns
+    are exact in bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = round_to_bf16_bits(np.where(np.isfinite(x), x, 0.0).astype(np.float32))
+    u = x.view(np.uint32)
+    inf = np.isinf(x)
+    bits[inf] = (u[inf] >> np.uint32(16)).astype(np.uint16)
+    return bits
