@@ -176,11 +176,11 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None, bias_block=None):
             lo, hi = int(inp.cu_seqlens[s]), int(inp.cu_seqlens[s + 1])
             qs, ks, vs = inp.q[lo:hi, h], inp.k[lo:hi, g], inp.v[lo:hi, g]
             dos = do[lo:hi, h] if do is not None else None
+        bb = bias_block(s, h) if bias_block is not None else None
         if do is None:
-            bb = bias_block(s, h) if bias_block is not None else None
             oracle.attention_head(qs, ks, vs, w.scale, w.causal, bias=bb)
         else:
-            oracle.attention_head_bwd(qs, ks, vs, dos, w.scale, w.causal)
+            oracle.attention_head_bwd(qs, ks, vs, dos, w.scale, w.causal, bias=bb)
         flops += (4 if do is None else 10) * w.d * visible_pairs(lens_q[s], lens_k[s], w.causal)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -416,7 +416,7 @@ def main(argv=None):
             if st != 0:
                 raise RuntimeError(f"fa_fwd_window failed: {fa.fa_last_error()}")
     bias_t = None
-    if args.bias != "none" and args.which == "fwd":
+    if args.bias != "none" and args.which in ("fwd", "bwd"):
         if w.dtype != "bf16" or w.packed or args.window >= 0:
             print("--bias needs a fixed-length bf16 workload and no window", file=sys.stderr)
             return 2
@@ -451,10 +451,17 @@ def main(argv=None):
         dsum = torch.empty_like(lse)
 
         def bwd_step():
-            st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                           dsum.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d, w.scale, int(w.causal),
-                           cu_ptr, sptr)
+            if bias_t is not None:
+                st = fa.fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), dsum.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d,
+                                    w.scale, int(w.causal), bias_t.data_ptr(), sb, sh, sr, cu_ptr,
+                                    sptr)
+            else:
+                st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), dsum.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d,
+                               w.scale, int(w.causal), cu_ptr, sptr)
             if st != 0:
                 raise RuntimeError(f"fa_bwd failed: {fa.fa_status_string(st)}: "
                                    f"{fa.fa_last_error()}")

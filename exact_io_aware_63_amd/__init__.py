@@ -5,7 +5,7 @@ HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
 The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_fwd_window``, ``fa_fwd_bias``,
-``fa_bwd``, ``fa_bwd_window``, ``fa_fwd_splitkv``, ``fa_status_string``,
+``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
 wrapper that checks torch tensors, allocates O and LSE with torch and calls
@@ -57,6 +57,10 @@ _lib.fa_fwd_bias.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
 _lib.fa_bwd.restype = ctypes.c_int
+_lib.fa_bwd_bias.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
+                             [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p])
+_lib.fa_bwd_bias.restype = ctypes.c_int
 _lib.fa_bwd_window.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 +
                                [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_void_p, ctypes.c_void_p])
@@ -75,6 +79,7 @@ _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
+            "fa_bwd_bias",
             "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_status_string",
             "fa_last_error", "fa_version")
 
@@ -254,13 +259,22 @@ def fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, 
                               int(causal), window_left, window_right, cu_seqlens, stream)
 
 
+def fa_bwd_bias(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                bias, bias_stride_b, bias_stride_h, bias_stride_row, cu_seqlens, stream) -> int:
+    """C ``fa_bwd_bias``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_bwd_bias(q, k, v, o, do, lse, dq, dk, dv, dsum, B, Hq, Hkv, Nq, Nk, d, scale,
+                            int(causal), bias, bias_stride_b, bias_stride_h, bias_stride_row,
+                            cu_seqlens, stream)
+
+
 def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_seqlens=None,
-                  max_seqlen=None, stream=None, window=None):
+                  max_seqlen=None, stream=None, window=None, bias=None):
     """Gradients (dQ, dK, dV) of attention through the C ABI (bf16 only).
 
     Tensors as ``attention_fwd`` takes and returns them (``o`` and ``lse``
-    from the forward call on the same inputs), ``do`` shaped like ``o``.
-    Allocates dQ, dK, dV and the float32 Dsum scratch with torch.
+    from the forward call on the same inputs, with the same ``window`` or
+    ``bias``), ``do`` shaped like ``o``. Allocates dQ, dK, dV and the
+    float32 Dsum scratch with torch.
     """
     import torch
 
@@ -295,7 +309,15 @@ def attention_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale=None, cu_s
     dsum = torch.empty_like(lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if window is not None:
+    if bias is not None:
+        if window is not None:
+            raise ValueError("a window and a bias do not combine; write the window into the bias")
+        sb, sh, sr = bias_strides(bias, B, Hq, Nq, Nk)
+        st = _lib.fa_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), dsum.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                              int(bool(causal)), bias.data_ptr(), sb, sh, sr, cu_ptr, stream)
+    elif window is not None:
         st = _lib.fa_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                 dv.data_ptr(), dsum.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),

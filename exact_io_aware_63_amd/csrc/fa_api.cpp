@@ -215,12 +215,13 @@ int validate_bwd(const void* Q, const void* K, const void* V, const void* O, con
 int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
             const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq, int Hkv,
             int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
-            void* stream, int win_left = -1, int win_right = -1) {
+            void* stream, int win_left = -1, int win_right = -1, const BiasArg* bias = nullptr) {
   g_last_error[0] = '\0';
   bool noop = false;
   int st = validate_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale,
                         cu_seqlens, &noop);
   if (st != FA_OK || noop) return st;
+  if (bias != nullptr && (st = validate_bias(*bias, Nk)) != FA_OK) return st;
   st = check_device();
   if (st != FA_OK) return st;
   fa::BwdParams p;
@@ -246,6 +247,10 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   p.causal = causal ? 1 : 0;
   p.win_left = win_left < 0 ? -1 : win_left;
   p.win_right = win_right < 0 ? -1 : win_right;
+  p.bias = bias ? bias->ptr : nullptr;
+  p.bias_sb = bias ? bias->sb : 0;
+  p.bias_sh = bias ? bias->sh : 0;
+  p.bias_sr = bias ? bias->sr : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 64)
@@ -369,6 +374,16 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
                   int window_right, const int32_t* cu_seqlens, void* stream) {
   return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
                  cu_seqlens, stream, window_left, window_right);
+}
+
+int fa_bwd_bias(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, void* dQ, void* dK, void* dV, float* Dsum, int B, int Hq,
+                int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* bias,
+                int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_row,
+                const int32_t* cu_seqlens, void* stream) {
+  const BiasArg b{bias, bias_stride_b, bias_stride_h, bias_stride_row};
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, Dsum, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 cu_seqlens, stream, -1, -1, &b);
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {

@@ -34,6 +34,11 @@
 // The causal mask is top-left (key j visible to query i iff j <= i, indices
 // local to the batch entry or sequence); blocks entirely above the diagonal
 // are skipped per wave, and partial blocks are masked element by element.
+// With an additive bias B (the BIAS variants) the recomputed probabilities
+// are P = exp(scale Q K^T + B - LSE), the LSE being the forward's with the
+// same bias; each lane loads the bias values of its own score registers
+// before the score MFMAs of a block. A row that saw no finite score in the
+// forward (LSE = -inf) gets P = 0 on every pair.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -188,7 +193,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdParams p) {
 // dK, dV
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL, bool WIN>
+// Exponent offset of a row: -LSE in base 2, or -inf for a row with
+// LSE = -inf when a bias is present (its pairs may be visible with B = -inf,
+// and every probability of the row is 0).
+template <bool BIAS>
+__device__ __forceinline__ float neg_lse2(float lse) {
+  if constexpr (BIAS) return lse == -INFINITY ? -INFINITY : -lse * kLog2e;
+  return -lse * kLog2e;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(u16 x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p, int n_kt) {
   using T = Tile<D>;
@@ -294,6 +312,17 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
         if (p.win_right >= 0 && qs0 + 31 < kw0 - p.win_right) continue;
         if (p.win_left >= 0 && qs0 > kw0 + 31 + p.win_left) continue;
       }
+      // Bias of this lane's key against the block's 16 queries of this
+      // half-wave (indices clamped into the sequence; clamped values belong
+      // to invisible pairs and are never used).
+      u16 bias_v[16];
+      if constexpr (BIAS) {
+        const u16* bgh = static_cast<const u16*>(p.bias) + b * p.bias_sb +
+                         head_of(it) * p.bias_sh + min(key, sb.Lk - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          bias_v[r] = bgh[static_cast<long>(min(qs0 + mrow(r, h2), sb.Lq - 1)) * p.bias_sr];
+      }
       // S = Q K^T and dP = dO V^T: lane = key, register r = query qs0 + mrow(r)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -315,7 +344,9 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
           const int r = 4 * g4 + e;
           const int q = qs0 + mrow(r, h2);
           const bool vis = visible<CAUSAL, WIN>(p, q, key, sb.Lq, sb.Lk);
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e] * kLog2e));
+          float off = neg_lse2<BIAS>(lv[e]);
+          if constexpr (BIAS) off = __builtin_fmaf(bf16_bits_to_float(bias_v[r]), kLog2e, off);
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, off));
           pr[r] = vis ? pe : 0.f;
           dsr[r] = pr[r] * (dp[r] - dvv[e]);
         }
@@ -359,7 +390,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
 // dQ
 // ---------------------------------------------------------------------------
 
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdParams p, int n_qt) {
   using T = Tile<D>;
@@ -409,7 +440,13 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
     dof[cc] = as_bf16x8(c);
   }
   const RowIndex ri = row_index(p, sb, b, h);
-  const float lse2 = qrow < sb.Lq ? p.lse[ri.at(qrow)] * kLog2e : 0.f;
+  const float nlse2 = qrow < sb.Lq ? neg_lse2<BIAS>(p.lse[ri.at(qrow)]) : 0.f;
+  // this lane's bias row (clamped into the sequence), 4 * h2 keys in: a run
+  // of 4 keys starts at every multiple of 4 and never crosses the row's end
+  const u16* brow = nullptr;
+  if constexpr (BIAS)
+    brow = static_cast<const u16*>(p.bias) + b * p.bias_sb + h * p.bias_sh +
+           static_cast<long>(min(qrow, sb.Lq - 1)) * p.bias_sr + 4 * h2;
   const float drow = qrow < sb.Lq ? p.dsum[ri.at(qrow)] : 0.f;
   const float c = p.scale_log2;
 
@@ -451,6 +488,14 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
         if (p.win_right >= 0 && ks0 > wq0 + 31 + p.win_right) break;
         if (p.win_left >= 0 && ks0 + 31 < wq0 - p.win_left) continue;
       }
+      // bias of keys ks0 + 8g + 4*h2 + (0..3) = registers 4g .. 4g+3
+      u32x2 bias_v[4];
+      if constexpr (BIAS) {
+        const int kmax = ((sb.Lk - 1) & ~3) - 4 * h2;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bias_v[g] = *reinterpret_cast<const u32x2*>(brow + min(ks0 + 8 * g, kmax));
+      }
       // S^T = K Q^T and dP^T = V dO^T: lane = query, register r = key ks0 + mrow(r)
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
@@ -463,7 +508,13 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
       for (int r = 0; r < 16; ++r) {
         const int kk = ks0 + mrow(r, h2);
         const bool vis = visible<CAUSAL, WIN>(p, qrow, kk, sb.Lq, sb.Lk);
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -lse2));
+        float off = nlse2;
+        if constexpr (BIAS) {
+          const uint32_t wd = bias_v[r >> 2][(r >> 1) & 1];
+          off = __builtin_fmaf(__uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16)), kLog2e,
+                               off);
+        }
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, off));
         dst[r] = vis ? pe * (dpt[r] - drow) : 0.f;
       }
       // dQ^T += K^T dS^T over the 32 keys (two 16-chunks)
@@ -499,7 +550,7 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
 // An empty side launches nothing for it: with Nq == 0 the dK/dV kernel
 // still runs and writes zeros (no query sees any key), with Nk == 0 the dQ
 // kernel writes zeros.
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
 hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
   const long n_rows = static_cast<long>(p.batch) * p.nq * p.hq;
   if (n_rows > 0) {
@@ -509,7 +560,7 @@ hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qt = (p.nq + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN>),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN, BIAS>),
                        dim3(static_cast<unsigned>(n_qt) * p.hq * p.batch), dim3(kThreads), 0,
                        stream, p, n_qt);
     const hipError_t e2 = hipGetLastError();
@@ -517,7 +568,7 @@ hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
   }
   if (p.nk > 0) {
     const int n_kt = (p.nk + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN>),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN, BIAS>),
                        dim3(static_cast<unsigned>(n_kt) * p.hkv * p.batch), dim3(kThreads), 0,
                        stream, p, n_kt);
     return hipGetLastError();
@@ -527,8 +578,10 @@ hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  if (p.win_left >= 0 || p.win_right >= 0) return launch_bwd_main<D, CAUSAL, true>(p, stream);
-  return launch_bwd_main<D, CAUSAL, false>(p, stream);
+  // the host never combines a bias with a window
+  if (p.bias != nullptr) return launch_bwd_main<D, CAUSAL, false, true>(p, stream);
+  if (p.win_left >= 0 || p.win_right >= 0) return launch_bwd_main<D, CAUSAL, true, false>(p, stream);
+  return launch_bwd_main<D, CAUSAL, false, false>(p, stream);
 }
 
 #if !defined(FA_BF16_D) || !defined(FA_BF16_CAUSAL)

@@ -66,6 +66,10 @@ struct BwdParams {
   int causal;
   int win_left;               // sliding window as FwdParams (-1: unbounded)
   int win_right;
+  const void* bias;           // additive bias as FwdParams, or nullptr
+  long bias_sb;
+  long bias_sh;
+  long bias_sr;
 };
 
 // Launch the bf16 backward (D = rowsum(dO * O), then dQ, then dK and dV)

@@ -192,6 +192,18 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O,
                   int Nk, int d, float scale, int causal, int window_left,
                   int window_right, const int32_t* cu_seqlens, void* stream);
 
+/* fa_bwd for the biased forward of fa_fwd_bias: the same bias (bias and
+ * strides as fa_fwd_bias; LSE and O from fa_fwd_bias with this bias). The
+ * probabilities are recomputed as P = exp(scale Q K^T + B - LSE); a row
+ * whose LSE is -inf (no finite biased score) contributes nothing. No
+ * gradient with respect to B is formed. */
+int fa_bwd_bias(const void* Q, const void* K, const void* V, const void* O,
+                const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                float* Dsum, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, const void* bias, int64_t bias_stride_b,
+                int64_t bias_stride_h, int64_t bias_stride_row,
+                const int32_t* cu_seqlens, void* stream);
+
 /*
  * Split-K/V attention forward for decode-shaped problems, bf16: the same
  * function as fa_fwd (fixed-length layout, same mask and grouping) for few

@@ -27,7 +27,7 @@ def fa():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
-         "fa_fwd_splitkv",
+         "fa_bwd_bias", "fa_fwd_splitkv",
          "fa_fwd_splitkv_workspace_bytes",
          "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -230,6 +230,31 @@ def test_bwd_one_sided_and_full_calls_reach_the_device(fa, kw):
 def _ws(B=2, Hq=8, Nq=1, d=64, n=4):
     rows = B * Hq * Nq * n
     return (rows * d * 4 + 255) // 256 * 256 + rows * 4
+
+
+def _call_bwd_bias(fa, bias=P, sb=0, sh=64, sr=8, **kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return fa.fa_bwd_bias(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                          a["dv"], a["dsum"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                          a["scale"], a["causal"], bias, sb, sh, sr, a["cu"], a["stream"])
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_BIAS[:8] + [
+    ("bwd_checks_still_apply", dict(dq=0), -1), ("bwd_alignment", dict(dsum=P + 4), -4)],
+    ids=[b[0] for b in BAD_BIAS[:8]] + ["bwd_checks_still_apply", "bwd_alignment"])
+def test_bwd_bias_rejects_bad_arguments(fa, name, kw, status):
+    st = _call_bwd_bias(fa, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error()
+
+
+def test_bwd_bias_noop_and_no_gpu(fa):
+    import torch
+    assert _call_bwd_bias(fa, B=0, bias=0) == 0
+    assert _call_bwd_bias(fa, Nq=0, Nk=0) == 0
+    if not torch.cuda.is_available():
+        assert _call_bwd_bias(fa) == fa.FA_ERR_HIP
 
 
 def test_splitkv_workspace_size(fa):

@@ -46,29 +46,35 @@ def _draw_do(shape, seed):
     return W.bf16_bits_to_f32(bits), bits
 
 
-def _run(inp, do_bits, causal, scale, window=None):
-    """GPU forward then backward; returns float64 numpy (dq, dk, dv)."""
+def _run(inp, do_bits, causal, scale, window=None, bias=None):
+    """GPU forward then backward; returns float64 numpy (dq, dk, dv).
+    ``bias``: a workloads.Bias, passed to both passes."""
     import torch
 
     import exact_io_aware_63_amd as fa
     q, k, v, cu = to_device(inp)
     ms = inp.max_seqlen if cu is not None else None
+    bt = None
+    if bias is not None:
+        bt = torch.from_numpy(bias.bits.view(np.int16)).view(torch.bfloat16).to(q.device)
     o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cu, max_seqlen=ms,
-                              window=window)
+                              window=window, bias=bt)
     do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(q.device)
     dq, dk, dv = fa.attention_bwd(q, k, v, o, lse, do, causal=causal, scale=scale, cu_seqlens=cu,
-                                  max_seqlen=ms, window=window)
+                                  max_seqlen=ms, window=window, bias=bt)
     torch.cuda.synchronize()
     return tuple(t.float().cpu().double().numpy() for t in (dq, dk, dv))
 
 
-def _head_terms(qh, kh, vh, doh, scale, causal, rows=None, window=None):
+def _head_terms(qh, kh, vh, doh, scale, causal, rows=None, window=None, bias_block=None):
     """P and dPa + Da (module docstring) of the given rows of one head
     (fp64; P from the definition, as the oracle forms it)."""
     lq, lk = qh.shape[0], kh.shape[0]
     rows = np.arange(lq) if rows is None else np.asarray(rows)
-    sc = np.where(oracle.visible_mask(rows, lk, causal, window), oracle.scores(qh[rows], kh, scale),
-                  -np.inf)
+    sc = oracle.scores(qh[rows], kh, scale)
+    if bias_block is not None:
+        sc = sc + np.asarray(bias_block[rows][:, :lk], dtype=np.float64)
+    sc = np.where(oracle.visible_mask(rows, lk, causal, window), sc, -np.inf)
     p, _, _ = oracle.softmax_rows(sc)
     dpa = np.abs(doh[rows]) @ np.abs(vh).T
     da = (p * dpa).sum(axis=1, keepdims=True)
@@ -92,14 +98,15 @@ def _heads(inp, do):
                 yield s, h, g, q[s, :, h], k[s, :, g], v[s, :, g], do[s, :, h]
 
 
-def _bounds_full(inp, do, scale, causal, window=None):
+def _bounds_full(inp, do, scale, causal, window=None, bias=None):
     """Elementwise magnitude sums of the module docstring, full tensors."""
     bq, bk, bv = (np.zeros(x.shape) for x in (inp.q, inp.k, inp.v))
     packed = inp.cu_seqlens is not None
     for s, h, g, qh, kh, vh, doh in _heads(inp, do):
         if qh.shape[0] == 0 or kh.shape[0] == 0:
             continue
-        p, w = _head_terms(qh, kh, vh, doh, scale, causal, window=window)
+        p, w = _head_terms(qh, kh, vh, doh, scale, causal, window=window,
+                           bias_block=oracle.bias_of(bias, s, h))
         a = abs(scale) * ((p * w) @ np.abs(kh))
         b = abs(scale) * ((p * w).T @ np.abs(qh))
         c = p.T @ np.abs(doh)
@@ -192,6 +199,38 @@ def test_bwd_window_parity(case):
     bounds = _bounds_full(inp, do, scale, causal, window=win)
     for nm, g, r, bd in zip(("dQ", "dK", "dV"), got, ref, bounds):
         _check(f"{name} {nm}", g, r, bd)
+
+
+BIAS_BWD = [
+    # name, B, Hq, Hkv, Nq, Nk, d, causal, lens, (bias entries, bias heads), sigma, extras
+    ("per_head", 2, 4, 2, 300, 300, 128, True, None, (2, 4), 1.0, {}),
+    ("head_shared_ragged", 1, 4, 1, 200, 333, 64, False, None, (1, 1), 2.0, {}),
+    ("key_padding_dead_rows", 2, 4, 2, 300, 300, 128, False, None, (2, 4), 1.0,
+     dict(key_lens=[300, 97], dead_rows=[(0, 1, 5), (1, 3, 299)])),
+    ("causal_dead_row0", 1, 4, 4, 257, 257, 64, True, None, (1, 1), 1.0,
+     dict(dead_rows=[(0, 0, 0)])),
+    ("large_bias", 1, 2, 1, 333, 200, 128, True, None, (1, 2), 8.0, {}),
+    ("packed", 1, 4, 2, 0, 0, 128, True, [1, 127, 300, 0, 513, 64], (6, 4), 1.0, {}),
+]
+
+
+@pytest.mark.parametrize("case", BIAS_BWD, ids=[c[0] for c in BIAS_BWD])
+def test_bwd_bias_parity(case):
+    name, b, hq, hkv, nq, nk, d, causal, lens, (be, bh), sigma, extra = case
+    say(f"[case] bwd bias {name}")
+    seed = zlib.crc32(("bwd bias " + name).encode())
+    inp = W.draw(len(lens) if lens else b, hq, hkv, nq, nk, d, "bf16", seed=seed, lens=lens)
+    rows = inp.max_seqlen if lens else nq
+    cols = inp.max_seqlen if lens else nk
+    bias = W.draw_bias(be, bh, rows, cols, seed + 2, sigma, **extra)
+    do, do_bits = _draw_do(inp.q.shape, seed + 1)
+    scale = 1.0 / math.sqrt(d)
+    got = _run(inp, do_bits, causal, scale, bias=bias)
+    ref = oracle.attention_bwd_ref(inp.q, inp.k, inp.v, do, scale, causal, inp.cu_seqlens,
+                                   bias=bias.values)
+    bounds = _bounds_full(inp, do, scale, causal, bias=bias.values)
+    for nm, g, r, bd in zip(("dQ", "dK", "dV"), got, ref, bounds):
+        _check(f"bias {name} {nm}", g, r, bd)
 
 
 def test_bwd_one_sided_calls_write_zeros():
