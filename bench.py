@@ -53,6 +53,7 @@ METRIC = "attention fwd TFLOP/s (bf16, causal, N=8192, d=128) and % of MFMA peak
 # MI355X published dense peaks (no sparsity): bf16/fp16 MFMA 2.5 PFLOP/s
 # (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s); HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_63_amd", "csrc", "fa_fwd_bf16.hip")
@@ -322,6 +323,9 @@ def main(argv=None):
                     help="forward with an additive bf16 bias (fa_fwd_bias): one [N, N] bias "
                          "shared by every head, or one per (entry, head); N(0, 1) values drawn "
                          "on the device from a seeded generator")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward with FP8 (e4m3) Q, K, V (fa_fwd_fp8, V^T pre-pass included): "
+                         "amax-scaled N(0, 1) inputs of the workload's shape")
     ap.add_argument("--decode-batch", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -415,6 +419,35 @@ def main(argv=None):
                                   int(w.causal), args.window, -1, cu_ptr, sptr)
             if st != 0:
                 raise RuntimeError(f"fa_fwd_window failed: {fa.fa_last_error()}")
+    fp8_x = None
+    if args.fp8:
+        if args.which != "fwd" or w.packed or w.d != 128 or args.window >= 0 or args.bias != "none":
+            print("--fp8 needs the forward pass on a fixed-length d=128 workload, no window or "
+                  "bias", file=sys.stderr)
+            return 2
+        fp8_x = W.draw_fp8(w.batch, w.hq, w.hkv, w.n, w.n, w.d, 1000 + w.wid,
+                           (w.sigma_q, w.sigma_k, w.sigma_v))
+        q8, k8, v8 = (torch.from_numpy(b).to(dev) for b in (fp8_x.q_bits, fp8_x.k_bits,
+                                                             fp8_x.v_bits))
+        ws_bytes = fa.fa_fwd_fp8_workspace_bytes(B, w.hkv, Nk)
+        ws8 = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        del q, k, v
+        torch.cuda.synchronize()
+
+        def fwd_step():  # noqa: F811  (the fp8 forward replaces the plain one)
+            st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, w.hq, w.hkv, Nq, Nk, w.d, w.scale,
+                               fp8_x.q_descale, fp8_x.k_descale, fp8_x.v_descale, int(w.causal),
+                               ws8.data_ptr(), ws_bytes, sptr)
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_fp8 failed: {fa.fa_last_error()}")
+        # the oracle's baseline runs on the dequantized values of these inputs
+        import oracle as _oracle_for_baseline
+        inp = W.Inputs(_oracle_for_baseline.e4m3_value(fp8_x.q_bits) * fp8_x.q_descale,
+                       _oracle_for_baseline.e4m3_value(fp8_x.k_bits) * fp8_x.k_descale,
+                       _oracle_for_baseline.e4m3_value(fp8_x.v_bits) * fp8_x.v_descale,
+                       "fp8", None, None)
+
     bias_t = None
     if args.bias != "none" and args.which in ("fwd", "bwd"):
         if w.dtype != "bf16" or w.packed or args.window >= 0:
@@ -512,7 +545,7 @@ def main(argv=None):
     win = (args.window, -1) if (args.window >= 0 and args.which == "fwd") else None
     flops = algorithmic_flops(lens_q, lens_k, w.hq, w.d, w.causal,
                               per_pair=10 if args.which == "bwd" else 4, window=win)
-    if win is not None or bias_t is not None:
+    if win is not None or bias_t is not None or fp8_x is not None:
         headline = False
     tq, tk = sum(lens_q), sum(lens_k)
     abytes = (algorithmic_bytes_bwd if args.which == "bwd" else algorithmic_bytes)(
@@ -521,7 +554,11 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(np.mean(per_launch_ms))
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    if w.dtype == "bf16":
+    if fp8_x is not None:
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None}
+        dtype_name = "fp8 e4m3 (float32 softmax, bf16 O)"
+    elif w.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": recorded_traffic() if (headline and args.which == "fwd") else None}
@@ -533,7 +570,8 @@ def main(argv=None):
         "metric": (METRIC if (headline and args.which == "fwd")
                    else f"attention {args.which} TFLOP/s ({w.name}"
                         f"{f', window {args.window}' if win is not None else ''}"
-                        f"{f', {args.bias} bias' if bias_t is not None else ''})"),
+                        f"{f', {args.bias} bias' if bias_t is not None else ''}"
+                        f"{', fp8 e4m3 inputs' if fp8_x is not None else ''})"),
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -550,11 +588,14 @@ def main(argv=None):
                    "seq_lens": lens_q if w.packed else None, "head_dim": w.d,
                    "causal": w.causal, "parallelism": "single GPU"},
         "roofline": roof,
-        "pct_of_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS if w.dtype == "bf16" else None,
+        "pct_of_mfma_peak": (100.0 * value / (PEAK_FP8_TFLOPS if fp8_x is not None
+                                               else PEAK_BF16_TFLOPS)
+                             if w.dtype == "bf16" else None),
         # the same against the peak at the clock amd-smi reads under this load
         # (4096 flop/clk/CU x 256 CUs x measured GFX clock)
         "pct_of_mfma_peak_at_measured_sclk": (
-            100.0 * value / (PEAK_BF16_TFLOPS * sclk["mean"] / 2400.0)
+            100.0 * value / ((PEAK_FP8_TFLOPS if fp8_x is not None else PEAK_BF16_TFLOPS)
+                             * sclk["mean"] / 2400.0)
             if (w.dtype == "bf16" and sclk) else None),
         "detail": {
             "alg_flops": flops,

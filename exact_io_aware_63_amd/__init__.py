@@ -5,7 +5,7 @@ HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
 The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_fwd_window``, ``fa_fwd_bias``,
-``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_status_string``,
+``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_fwd_fp8``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
 wrapper that checks torch tensors, allocates O and LSE with torch and calls
@@ -69,6 +69,11 @@ _lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
                                 [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
 _lib.fa_fwd_splitkv.restype = ctypes.c_int
+_lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float] * 4 +
+                            [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+_lib.fa_fwd_fp8.restype = ctypes.c_int
+_lib.fa_fwd_fp8_workspace_bytes.argtypes = [ctypes.c_int] * 3
+_lib.fa_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_fwd_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 5
 _lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [ctypes.c_int]
@@ -80,8 +85,8 @@ _lib.fa_version.restype = ctypes.c_int
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
             "fa_bwd_bias",
-            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_status_string",
-            "fa_last_error", "fa_version")
+            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_fp8",
+            "fa_fwd_fp8_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -154,6 +159,55 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlen
 def fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:
     """C ``fa_fwd_splitkv_workspace_bytes``."""
     return _lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale,
+               causal, workspace, workspace_bytes, stream) -> int:
+    """C ``fa_fwd_fp8``: pointers are integer device addresses (or 0 / None)."""
+    return _lib.fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale,
+                           v_descale, int(causal), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_fp8_workspace_bytes(B, Hkv, Nk) -> int:
+    """C ``fa_fwd_fp8_workspace_bytes``."""
+    return _lib.fa_fwd_fp8_workspace_bytes(B, Hkv, Nk)
+
+
+def attention_fwd_fp8(q, k, v, *, q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                      causal: bool = False, scale=None, stream=None):
+    """FP8 attention forward through the C ABI.
+
+    q [B, Nq, Hq, 128], k and v [B, Nk, Hkv, 128]: contiguous device tensors
+    of e4m3 codes (torch.uint8 or torch.float8_e4m3fn). The function is the
+    attention of the dequantized tensors (descale * codes). Allocates O
+    (bf16, q's shape), LSE (float32 [B, Hq, Nq]) and the workspace with
+    torch. Returns (O, LSE).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn)")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_fp8_workspace_bytes(B, Hkv, Nk)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, Hq, Hkv, Nq, Nk, d, float(scale), float(q_descale), float(k_descale),
+                         float(v_descale), int(bool(causal)), ws.data_ptr(), nbytes, stream)
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+    return out, lse
 
 
 def fa_status_string(status: int) -> str:

@@ -20,7 +20,7 @@ OBJ_DIR = os.path.join(os.path.dirname(PKG), "_build")
 SOURCES = [("fa_api.cpp", "fa_api", []), ("fa_fwd_fp32.hip", "fa_fwd_fp32", [])] + [
     (f"fa_{pas}_bf16.hip", f"fa_{pas}_bf16_d{d}_c{c}", [f"-DFA_BF16_D={d}", f"-DFA_BF16_CAUSAL={c}"])
     for pas in ("fwd", "bwd") for d in (128, 64) for c in (1, 0)] + [
-    ("fa_decode_bf16.hip", "fa_decode_bf16", [])]
+    ("fa_decode_bf16.hip", "fa_decode_bf16", []), ("fa_fwd_fp8.hip", "fa_fwd_fp8", [])]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

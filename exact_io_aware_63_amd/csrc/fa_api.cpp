@@ -328,6 +328,69 @@ int run_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE
   return FA_OK;
 }
 
+constexpr int kFp8D = 128;
+constexpr int kFp8Block = 64;       // keys per V^T tile
+constexpr size_t kFp8TileBytes = 8192;
+
+size_t fp8_workspace(int B, int Hkv, int Nk) {
+  const size_t nblk = (static_cast<size_t>(Nk) + kFp8Block - 1) / kFp8Block;
+  return static_cast<size_t>(B) * Hkv * nblk * kFp8TileBytes;
+}
+
+int run_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq, int Hkv,
+            int Nq, int Nk, int d, float scale, float q_descale, float k_descale,
+            float v_descale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B=%d, Nq=%d, Nk=%d must be >= 0", B, Nq, Nk);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_SHAPE, "Hq=%d and Hkv=%d must be > 0", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d != kFp8D) return fail(FA_ERR_UNSUPPORTED, "head width d=%d; the fp8 path takes 128", d);
+  if (!std::isfinite(scale) || !std::isfinite(q_descale) || !std::isfinite(k_descale) ||
+      !std::isfinite(v_descale))
+    return fail(FA_ERR_ARG, "scale and descale factors must be finite");
+  const double c = static_cast<double>(scale) * q_descale * k_descale * 1.4426950408889634;
+  if (!(std::fabs(c) <= 3.0e38)) return fail(FA_ERR_ARG, "scale * q_descale * k_descale overflows");
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (!Q || !O || !LSE || (Nk > 0 && (!K || !V || !workspace)))
+    return fail(FA_ERR_NULL, "Q, O, LSE (and with keys K, V, workspace) must be non-NULL");
+  if (!aligned(Q, 16) || (K && !aligned(K, 16)) || (V && !aligned(V, 16)) || !aligned(O, 16))
+    return fail(FA_ERR_ARG, "Q, K, V and O must be 16-byte aligned");
+  if (!aligned(LSE, 4)) return fail(FA_ERR_ARG, "LSE must be 4-byte aligned");
+  if (workspace && !aligned(workspace, 256))
+    return fail(FA_ERR_ARG, "workspace must be 256-byte aligned");
+  const size_t need = fp8_workspace(B, Hkv, Nk);
+  if (Nk > 0 && workspace_bytes < need)
+    return fail(FA_ERR_ARG, "workspace of %zu bytes is below the %zu the call needs",
+                workspace_bytes, need);
+  const int64_t n_qt = (static_cast<int64_t>(Nq) + 255) / 256;
+  const int64_t nblk = (static_cast<int64_t>(Nk) + kFp8Block - 1) / kFp8Block;
+  if (n_qt * Hq * static_cast<int64_t>(B) > 0x7fffffffLL ||
+      nblk * Hkv * static_cast<int64_t>(B) > 0x7fffffffLL)
+    return fail(FA_ERR_SHAPE, "problem exceeds the launch limits");
+  int st = check_device();
+  if (st != FA_OK) return st;
+  fa::Fp8Params p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.vt = workspace;
+  p.o = O;
+  p.lse = LSE;
+  p.batch = B;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.nq = Nq;
+  p.nk = Nk;
+  p.nblk = static_cast<int>(nblk);
+  p.c = static_cast<float>(c);
+  p.v_descale = v_descale;
+  p.causal = causal ? 1 : 0;
+  const hipError_t e = fa::launch_fwd_fp8(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +460,19 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    size_t workspace_bytes, void* stream) {
   return run_splitkv(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k, num_splits,
                      workspace, workspace_bytes, stream);
+}
+
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Nk) {
+  if (B <= 0 || Hkv <= 0 || Nk <= 0) return 0;
+  return fp8_workspace(B, Hkv, Nk);
+}
+
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+               int Hkv, int Nq, int Nk, int d, float scale, float q_descale, float k_descale,
+               float v_descale, int causal, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  return run_fp8(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale,
+                 causal, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

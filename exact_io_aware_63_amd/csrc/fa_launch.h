@@ -108,6 +108,30 @@ hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 extern template hipError_t launch_decode_bf16<64>(const DecodeParams&, hipStream_t);
 extern template hipError_t launch_decode_bf16<128>(const DecodeParams&, hipStream_t);
 
+// One FP8 (e4m3) attention-forward problem, already validated on the host:
+// fixed length, d = 128, Q [B, Nq, Hq, 128], K and V [B, Nk, Hkv, 128]
+// (bytes), O [B, Nq, Hq, 128] bf16, LSE [B, Hq, Nq].
+struct Fp8Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* vt;                   // workspace: [B, Hkv, nblk] V^T tiles of 8 KiB
+  void* o;
+  float* lse;
+  int batch;
+  int hq;
+  int hkv;
+  int nq;
+  int nk;
+  int nblk;                   // ceil(Nk / 64)
+  float c;                    // scale * dq * dk * log2(e)
+  float v_descale;            // dv
+  int causal;
+};
+
+// V^T pre-pass, then the forward kernel.
+hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
+
 // Launch the float32 kernel (d in {64, 128}).
 hipError_t launch_fwd_fp32(const FwdParams& p, hipStream_t stream);
 

@@ -238,6 +238,38 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O,
                    int num_splits, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * Attention forward with FP8 inputs: Q, K, V in OCP e4m3 (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities, 0x7f / 0xff
+ * are NaN) with one dequantization factor per tensor. The function is the
+ * attention of the dequantized inputs q = q_descale * Q, k = k_descale * K,
+ * v = v_descale * V: S = scale q k^T, P = softmax_row(S), O = P v, LSE as
+ * fa_fwd. The pages list FP8 as FlashAttention-3's low-precision variant
+ * and state that its speed has a precision cost ("Understanding
+ * FlashAttention Pt 1: Personal Notes", contents, section 5.6). The cost
+ * here is one rounding: the scores are exact products summed in float32;
+ * the probabilities are rounded to e4m3 for the P V product (an absolute
+ * error of at most 2^-4 P_ij, or 2^-16 of the row's largest weight when
+ * that is larger, per term); O is rounded once to bf16.
+ *   Q [B, Nq, Hq, 128], K, V [B, Nk, Hkv, 128] : device, e4m3 bytes,
+ *            16-byte aligned. Fixed length only; d must be 128.
+ *   O [B, Nq, Hq, 128] : device, bf16, 16-byte aligned.
+ *   LSE [B, Hq, Nq] : device, float32.
+ *   scale, q_descale, k_descale, v_descale : finite floats.
+ *   causal : top-left mask as fa_fwd.
+ *   workspace : device memory of at least fa_fwd_fp8_workspace_bytes(B,
+ *            Hkv, Nk) bytes, 256-byte aligned, owned by the caller; the call
+ *            writes V, transposed in 64-key tiles, there first (its contents
+ *            on return are unspecified). May be NULL when Nk == 0.
+ * B == 0 or Nq == 0 is a no-op. Errors as fa_fwd; FA_ERR_UNSUPPORTED for
+ * d != 128.
+ */
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Nk);
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+               float q_descale, float k_descale, float v_descale, int causal,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(int status);
 

@@ -434,3 +434,37 @@ def attention_bwd_picked(q, k, v, do, scale: float, causal: bool, q_picks, kv_pi
                 dv[sel] += p[:, cols].T @ doh[r]
                 dk[sel] += scale * (ds[:, cols].T @ qh[r])
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs
+# ---------------------------------------------------------------------------
+
+def e4m3_value(bits) -> np.ndarray:
+    """Values of OCP e4m3 codes (uint8) as float64, from the format's
+    definition: sign bit s, exponent field e (4 bits, bias 7), mantissa
+    field m (3 bits); e > 0 gives (-1)^s 2^(e-7) (1 + m/8), e = 0 gives the
+    subnormal (-1)^s 2^-6 (m/8); e = 15 with m = 7 is NaN (no infinities).
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    return np.where((e == 15) & (m == 7), np.nan, s * mag)
+
+
+def attention_fp8_ref(q_bits, k_bits, v_bits, q_descale: float, k_descale: float,
+                      v_descale: float, scale: float, causal: bool):
+    """Attention of FP8 inputs: the exact attention (``attention_ref``) of the
+    dequantized tensors q = q_descale * Q, k = k_descale * K,
+    v = v_descale * V, fixed-length layouts. The pages list FP8 only as
+    FlashAttention-3's low-precision variant ("Understanding FlashAttention
+    Pt 1", contents, section 5.6); reading: the inputs are e4m3 with one
+    dequantization factor per tensor, and the function computed is unchanged.
+    Returns (O, LSE) as float64."""
+    q = e4m3_value(q_bits) * float(q_descale)
+    k = e4m3_value(k_bits) * float(k_descale)
+    v = e4m3_value(v_bits) * float(v_descale)
+    return attention_ref(q, k, v, scale, causal)
+

@@ -641,6 +641,57 @@ def pin_bias_packed():
         _assert_close(pl[r], lse[h, cu[s] + i], 1e-15, "picked bias LSE")
 
 
+def pin_e4m3_codes():
+    """OCP e4m3 values fixed by the format: zero, the smallest subnormal
+    2^-9, the largest subnormal 7 * 2^-9, the smallest normal 2^-6, one,
+    1.875, two, the largest value 448, signs, and NaN at 0x7f / 0xff."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    got = A.e4m3_value(np.array(list(want), dtype=np.uint8))
+    _assert_close(got, np.array(list(want.values())), 0.0, "e4m3 codes")
+    assert np.isnan(A.e4m3_value(np.array([0x7F, 0xFF], dtype=np.uint8))).all(), "e4m3 NaN codes"
+    assert np.signbit(A.e4m3_value(np.array([0x80], dtype=np.uint8)))[0], "e4m3 negative zero"
+
+
+def pin_e4m3_library():
+    """All 256 e4m3 codes decode to torch's float8_e4m3fn values."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = A.e4m3_value(codes)
+    same = (got == lib) | (np.isnan(got) & np.isnan(lib))
+    assert same.all(), f"e4m3 codes differ at {np.nonzero(~same)[0][:8]}"
+
+
+def pin_fp8_descale_laws():
+    """The dequantization factors act on the function as the definition
+    says: q_descale * 2 is the same call as scale * 2 (so is k_descale),
+    v_descale scales O and leaves LSE; with descale 1, the call is the
+    attention of the decoded codes (Q = 0.5 everywhere gives uniform
+    weights: O = the mean of the visible values)."""
+    rng = _rng(51)
+    qb = rng.integers(0, 0x7E, (1, 6, 2, 8), dtype=np.uint8) | (rng.integers(0, 2, (1, 6, 2, 8),
+                                                                              dtype=np.uint8) << 7)
+    kb = rng.integers(0, 0x50, (1, 7, 1, 8), dtype=np.uint8)
+    vb = rng.integers(0, 0x7E, (1, 7, 1, 8), dtype=np.uint8)
+    for causal in (False, True):
+        o1, l1 = A.attention_fp8_ref(qb, kb, vb, 0.02, 0.03, 1.5, 0.4, causal)
+        o2, l2 = A.attention_fp8_ref(qb, kb, vb, 0.04, 0.03, 1.5, 0.2, causal)
+        o3, l3 = A.attention_fp8_ref(qb, kb, vb, 0.02, 0.06, 3.0, 0.2, causal)
+        _assert_close(o2, o1, 1e-14, "q_descale vs scale O")
+        _assert_close(l2, l1, 1e-13, "q_descale vs scale LSE")
+        _assert_close(o3, 2 * o1, 1e-13, "v_descale scales O")
+        _assert_close(l3, l1, 1e-13, "v_descale leaves LSE")
+    half = np.full((1, 5, 1, 4), 0x30, dtype=np.uint8)    # 0.5
+    vb = rng.integers(0, 0x60, (1, 5, 1, 4), dtype=np.uint8)
+    o, lse = A.attention_fp8_ref(half, np.zeros((1, 5, 1, 4), np.uint8), vb, 1.0, 1.0, 1.0, 0.7,
+                                 True)
+    vals = A.e4m3_value(vb)[0, :, 0]
+    for i in range(5):
+        _assert_close(o[0, i, 0], vals[:i + 1].mean(axis=0), 1e-13, "uniform fp8 rows")
+        _assert_close(lse[0, 0, i], math.log(i + 1), 1e-15, "uniform fp8 LSE")
+
+
 ALL_PINS = [
     pin_rows_sum_to_one, pin_single_key, pin_uniform_scores_mean, pin_two_key_closed_form,
     pin_permutation_invariance, pin_brute_force, pin_online_route, pin_causal_structure,
@@ -648,5 +699,6 @@ ALL_PINS = [
     pin_hard_max_limit, pin_library_sdpa, pin_empty_cases, pin_picked_rows,
     pin_window_wide_equals_plain, pin_window_zero_left_causal, pin_window_by_slicing,
     pin_window_brute_force, pin_bias_row_constant, pin_bias_log_weights, pin_bias_as_mask,
-    pin_bias_brute_force, pin_bias_library_sdpa, pin_bias_packed,
+    pin_bias_brute_force, pin_bias_library_sdpa, pin_bias_packed, pin_e4m3_codes,
+    pin_e4m3_library, pin_fp8_descale_laws,
 ]

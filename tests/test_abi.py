@@ -27,7 +27,7 @@ def fa():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
-         "fa_bwd_bias", "fa_fwd_splitkv",
+         "fa_bwd_bias", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes",
          "fa_fwd_splitkv_workspace_bytes",
          "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -310,4 +310,52 @@ def test_splitkv_valid_call_without_gpu_fails_cleanly(fa):
         pytest.skip("a GPU is present")
     assert _call_skv(fa) == fa.FA_ERR_HIP
     assert _call_skv(fa, Nk=0, k=0, v=0) == fa.FA_ERR_HIP  # no keys: O = 0, LSE = -inf to write
+
+
+# fa_fwd_fp8: fake addresses, workspace 256-byte aligned.
+GOOD_FP8 = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=4, Hkv=2, Nq=100, Nk=130, d=128, scale=0.1,
+                qd=0.5, kd=0.25, vd=2.0, causal=1, ws=P, wsb=1 << 20, stream=None)
+
+
+def _call_fp8(fa, **kw):
+    a = dict(GOOD_FP8)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                         a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"],
+                         a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fp8_workspace_size(fa):
+    assert fa.fa_fwd_fp8_workspace_bytes(2, 2, 130) == 2 * 2 * 3 * 8192
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 8, 8192) == 8 * 128 * 8192
+    assert fa.fa_fwd_fp8_workspace_bytes(0, 2, 10) == 0
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 0) == 0
+
+
+BAD_FP8 = [
+    ("null_q", dict(q=0), -1), ("null_k", dict(k=0), -1), ("null_v", dict(v=0), -1),
+    ("null_o", dict(o=0), -1), ("null_lse", dict(lse=0), -1), ("null_ws", dict(ws=0), -1),
+    ("neg_batch", dict(B=-1), -2), ("hq_not_multiple", dict(Hq=6, Hkv=4), -2),
+    ("d_64", dict(d=64), -3), ("d_256", dict(d=256), -3),
+    ("scale_nan", dict(scale=math.nan), -4), ("qd_inf", dict(qd=math.inf), -4),
+    ("vd_nan", dict(vd=math.nan), -4), ("c_overflow", dict(scale=1e30, qd=1e10, kd=1.0), -4),
+    ("misaligned_q", dict(q=P + 8), -4), ("misaligned_o", dict(o=P + 4), -4),
+    ("misaligned_ws", dict(ws=P + 16), -4), ("workspace_small", dict(wsb=2 * 2 * 3 * 8192 - 1), -4),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_FP8, ids=[b[0] for b in BAD_FP8])
+def test_fp8_rejects_bad_arguments(fa, name, kw, status):
+    st = _call_fp8(fa, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error()
+
+
+def test_fp8_noop_and_no_gpu(fa):
+    import torch
+    assert _call_fp8(fa, B=0, q=0, k=0, v=0, o=0, lse=0, ws=0) == 0
+    assert _call_fp8(fa, Nq=0) == 0
+    if not torch.cuda.is_available():
+        assert _call_fp8(fa) == fa.FA_ERR_HIP
+        assert _call_fp8(fa, Nk=0, k=0, v=0, ws=0, wsb=0) == fa.FA_ERR_HIP
 

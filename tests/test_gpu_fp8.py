@@ -1,0 +1,223 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8) against the fp64 oracle of
+the dequantized inputs.
+
+Tolerance, from the arithmetic of the kernel and of the fp8 matrix
+instruction:
+
+* P rounding. The normaliser l is the float32 sum of the unrounded weights
+  w = 2^(x - m + 6); each weight is rounded to e4m3 before the P V product:
+  at most 2^-4 w for a normal and 2^-10 (half the subnormal step) below
+  2^-6, while the row's largest weight, hence l, is at least 2^6.
+* Accumulation inside v_mfma_f32_32x32x64_f8f6f4. Its 64-product dot
+  products are not exact: measured with one wave on the GPU (B = 1, rows of
+  A with known sums), low bits of products next to a larger one in the same
+  group of 8 are dropped (448 + 63 * 2^-9 comes out as 448.109375, the 7
+  small terms grouped with 448 lost; 256 + 63 * 0.28125 loses 7 * 2^-6),
+  each term losing less than 2^-13 of its group's largest product, so an
+  instruction's error is below 7 * 2^-13 * sum_k |a_k b_k| < 2^-10 sum_k
+  |a_k b_k|. Over random e4m3 operands (512 waves, 1024 outputs each) the
+  largest error seen was 2^-11.8 sum_k |a_k b_k|. Hence eps = 2^-10.
+  Partial sums across instructions are float32.
+
+With Pabs_i = sum_j P_ij |V_j| (the oracle's attention of |V|), Vsum_i =
+sum of |V_j| over the keys row i sees, and Sabs_ij = |scale| |q_i|.|k_j|
+(the absolute score sum), elementwise
+
+    |O_gpu - O_ref|_i <= 2^-4 Pabs_i + 2^-16 Vsum_i                  (P rounding)
+                         + eps (1 + 2^-4) Pabs_i                      (P V sums)
+                         + eps sum_j P_ij Sabs_ij (|V_j| + |O_i|)     (score sums)
+                         + 2^-8 |O_ref|_i + 1e-6                      (bf16 O),
+    |LSE_gpu - LSE_ref|_i <= eps sum_j P_ij Sabs_ij + 1e-5 (1 + |LSE_i|).
+
+When every score is an integer and the scale is ln 2 (the "signs" inputs:
+4 entries of +-1 per row of Q and K), every weight is a power of two within
+e4m3's exact range and every score sum is exact, so the P rounding and score
+terms vanish and only the P V sums and the bf16 rounding remain.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_63_amd  # noqa: F401
+
+
+def _dev(bits):
+    import torch
+    return torch.from_numpy(bits).to("cuda")
+
+
+def _run(x, causal, scale):
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    o, lse = fa.attention_fwd_fp8(_dev(x.q_bits), _dev(x.k_bits), _dev(x.v_bits),
+                                  q_descale=x.q_descale, k_descale=x.k_descale,
+                                  v_descale=x.v_descale, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def _deq(x):
+    return (oracle.e4m3_value(x.q_bits) * x.q_descale, oracle.e4m3_value(x.k_bits) * x.k_descale,
+            oracle.e4m3_value(x.v_bits) * x.v_descale)
+
+
+EPS = 2.0 ** -10
+
+
+def _row_terms(qh, kh, vh, scale, causal, rows, o_rows):
+    """Bound terms of the given rows of one head (fp64): Pabs, Vsum,
+    sum_j P Sabs (|V_j| + |O_i|) per column, and sum_j P Sabs."""
+    lk = kh.shape[0]
+    vis = oracle.visible_mask(rows, lk, causal)
+    p, _, _ = oracle.softmax_rows(np.where(vis, oracle.scores(qh[rows], kh, scale), -np.inf))
+    sabs = abs(scale) * (np.abs(qh[rows]) @ np.abs(kh).T)
+    ps = p * sabs
+    va = np.abs(vh)
+    return (p @ va, vis.astype(np.float64) @ va,
+            ps @ va + ps.sum(axis=1, keepdims=True) * np.abs(o_rows), ps.sum(axis=1))
+
+
+def _bounds(q, k, v, scale, causal, o_ref, lse_ref, exact):
+    """Elementwise O and LSE bounds of the module docstring, fixed-length
+    layouts (q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d])."""
+    bo = np.zeros_like(o_ref)
+    bl = np.zeros_like(lse_ref)
+    bsz, nq, hq, _ = q.shape
+    hkv = k.shape[2]
+    rows = np.arange(nq)
+    for b in range(bsz):
+        for h in range(hq):
+            g = oracle.kv_head_of(h, hq, hkv)
+            pabs, vsum, psv, ps = _row_terms(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal,
+                                             rows, o_ref[b, :, h])
+            round_p = 0.0 if exact else 2.0 ** -4 * pabs + 2.0 ** -16 * vsum
+            bo[b, :, h] = (round_p + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
+                           2.0 ** -8 * np.abs(o_ref[b, :, h]) + 1e-6)
+            bl[b, h] = EPS * ps + 1e-5 * (1 + np.abs(np.where(np.isfinite(lse_ref[b, h]),
+                                                              lse_ref[b, h], 0.0)))
+    return bo, bl
+
+
+def _check(name, o, lse, o_ref, lse_ref, bo, bl):
+    err = np.abs(o - o_ref)
+    assert np.all(np.isfinite(o)), f"{name}: non-finite O"
+    ratio = float((err / bo).max()) if err.size else 0.0
+    same_inf = np.isinf(lse) & np.isinf(lse_ref) & (np.sign(lse) == np.sign(lse_ref))
+    el = np.where(same_inf, 0.0, np.abs(lse - lse_ref))
+    lratio = float((el / bl).max()) if el.size else 0.0
+    say(f"[fp8 parity] {name}: max|dO| {float(err.max()) if err.size else 0:.3e}, "
+        f"O err/bound {ratio:.3f}, max|dLSE| {float(el.max()) if el.size else 0:.2e}, "
+        f"LSE err/bound {lratio:.3f}")
+    assert ratio <= 1.0, f"{name}: O error exceeds the bound (ratio {ratio:.3f})"
+    assert lratio <= 1.0, f"{name}: LSE error exceeds the bound (ratio {lratio:.3f})"
+
+
+CASES = [
+    # name, B, Hq, Hkv, Nq, Nk, causal, mode, sigma
+    ("signs_causal", 1, 8, 2, 1500, 1500, True, "signs", (1.0, 1.0, 1.0)),
+    ("signs_full_ragged", 2, 4, 4, 600, 333, False, "signs", (1.0, 1.0, 1.0)),
+    ("normal_causal", 2, 4, 2, 700, 700, True, "normal", (1.0, 1.0, 1.0)),
+    ("normal_full_ragged", 1, 8, 2, 333, 517, False, "normal", (1.0, 1.0, 1.0)),
+    ("wide_scores_rescale", 1, 4, 4, 1000, 1000, True, "normal", (3.0, 3.0, 1.0)),
+    ("tail_130", 1, 4, 1, 130, 130, True, "normal", (1.0, 1.0, 1.0)),
+    ("tiny", 1, 2, 1, 1, 3, False, "normal", (1.0, 1.0, 1.0)),
+    ("rows_past_keys", 1, 2, 2, 300, 70, True, "normal", (1.0, 1.0, 1.0)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_parity(case):
+    name, b, hq, hkv, nq, nk, causal, mode, sigma = case
+    say(f"[case] fp8 {name}")
+    x = W.draw_fp8(b, hq, hkv, nq, nk, 128, zlib.crc32(name.encode()), sigma, mode)
+    scale = math.log(2.0) if mode == "signs" else 1.0 / math.sqrt(128)
+    o, lse = _run(x, causal, scale)
+    q, k, v = _deq(x)
+    o_ref, lse_ref = oracle.attention_fp8_ref(x.q_bits, x.k_bits, x.v_bits, x.q_descale,
+                                              x.k_descale, x.v_descale, scale, causal)
+    _check(name, o, lse, o_ref, lse_ref, *_bounds(q, k, v, scale, causal, o_ref, lse_ref,
+                                                  mode == "signs"))
+
+
+def test_fp8_no_keys():
+    """Nk = 0: every row gets O = 0 and LSE = -inf (no workspace needed)."""
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    say("[case] fp8 no keys")
+    q = torch.full((1, 40, 2, 128), 0x38, dtype=torch.uint8, device="cuda")
+    kv = torch.empty((1, 0, 1, 128), dtype=torch.uint8, device="cuda")
+    o, lse = fa.attention_fwd_fp8(q, kv, kv, causal=False)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_fp8_deterministic_and_negative_scale():
+    """Repeated calls agree bitwise; a negative scale is the attention of the
+    negated scores (the oracle with the same scale)."""
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    say("[case] fp8 determinism, negative scale")
+    x = W.draw_fp8(1, 4, 2, 500, 500, 128, 91)
+    args = [_dev(x.q_bits), _dev(x.k_bits), _dev(x.v_bits)]
+    kw = dict(q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale, causal=True)
+    o1, l1 = fa.attention_fwd_fp8(*args, **kw)
+    o2, l2 = fa.attention_fwd_fp8(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o, lse = _run(x, True, -0.2)
+    q, k, v = _deq(x)
+    o_ref, lse_ref = oracle.attention_fp8_ref(x.q_bits, x.k_bits, x.v_bits, x.q_descale,
+                                              x.k_descale, x.v_descale, -0.2, True)
+    _check("negative scale", o, lse, o_ref, lse_ref, *_bounds(q, k, v, -0.2, True, o_ref, lse_ref,
+                                                              False))
+
+
+def test_fp8_full_size_sampled():
+    """Causal GQA 32/8 heads, N = 8192, d = 128 (the bf16 workload's shape)
+    with amax-scaled N(0, 1) inputs; rows sampled at tile edges and at
+    random, each formed whole by the oracle, against the bound."""
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    say("[case] fp8 full size: causal GQA 32/8, N=8192, d=128")
+    w = W.WORKLOADS[4]
+    x = W.draw_fp8(1, w.hq, w.hkv, w.n, w.n, w.d, 4008)
+    o, lse = fa.attention_fwd_fp8(_dev(x.q_bits), _dev(x.k_bits), _dev(x.v_bits),
+                                  q_descale=x.q_descale, k_descale=x.k_descale,
+                                  v_descale=x.v_descale, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4008)
+    rows = sorted({0, 1, 63, 64, 255, 256, 4095, 4096, w.n - 2, w.n - 1} |
+                  set(rng.integers(0, w.n, 14).tolist()))
+    picks = np.array([(0, int(rng.integers(w.hq)), i) for i in rows])
+    q, k, v = _deq(x)
+    ro, rl = oracle.attention_picked(q, k, v, w.scale, True, picks)
+    bo = np.zeros_like(ro)
+    bl = np.zeros_like(rl)
+    for n, (s, h, i) in enumerate(picks):
+        g = oracle.kv_head_of(int(h), w.hq, w.hkv)
+        pabs, vsum, psv, ps = _row_terms(q[s, :, h], k[s, :, g], v[s, :, g], w.scale, True,
+                                         np.array([i]), ro[n:n + 1])
+        bo[n] = (2.0 ** -4 * pabs + 2.0 ** -16 * vsum + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
+                 2.0 ** -8 * np.abs(ro[n:n + 1]) + 1e-6)[0]
+        bl[n] = EPS * ps[0] + 1e-5 * (1 + abs(rl[n]))
+    go = o[0, picks[:, 2], picks[:, 1]].float().cpu().double().numpy()
+    gl = lse[0, picks[:, 1], picks[:, 2]].cpu().double().numpy()
+    _check("full size sampled", go, gl, ro, rl, bo, bl)

@@ -99,7 +99,26 @@ def _bias_of_swapped(bias, s, h):
     return b[h if b.shape[0] > 1 else 0, s if b.shape[1] > 1 else 0]
 
 
+_orig_e4m3 = A.e4m3_value
+
+
+def _e4m3_bias8(bits):
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> 3) & 0xF, (b & 7).astype(np.float64)
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 8), np.ldexp(m / 8.0, -7))
+    return np.where(b & 0x80, -1.0, 1.0) * mag
+
+
+def _e4m3_no_subnormals(bits):
+    v = _orig_e4m3(bits)
+    e = (np.asarray(bits, dtype=np.uint8) >> 3) & 0xF
+    return np.where(e == 0, 0.0, v)
+
+
 MUTANTS = {
+    "e4m3_exponent_bias_8": ("e4m3_value", _e4m3_bias8),
+    "e4m3_subnormals_flushed": ("e4m3_value", _e4m3_no_subnormals),
+    "e4m3_sign_dropped": ("e4m3_value", lambda bits: np.abs(_orig_e4m3(bits))),
     "bias_ignored": ("attention_head", _head_with_bias(lambda b, scale: np.zeros_like(b))),
     "bias_transposed": ("attention_head", _head_with_bias(lambda b, scale: b.T)),
     "bias_negated": ("attention_head", _head_with_bias(lambda b, scale: -b)),

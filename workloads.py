@@ -191,3 +191,62 @@ def round_to_bf16_bits_inf(x: np.ndarray) -> np.ndarray:
     inf = np.isinf(x)
     bits[inf] = (u[inf] >> np.uint32(16)).astype(np.uint16)
     return bits
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """FP8 (OCP e4m3) inputs: the codes of Q, K, V (uint8, fixed-length
+    layouts) and one dequantization factor per tensor."""
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    q_descale: float
+    k_descale: float
+    v_descale: float
+
+
+def to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values (finite, |x| <= 448) to e4m3 codes with torch's
+    float8_e4m3fn cast (round to nearest, ties to even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def draw_fp8(batch: int, hq: int, hkv: int, nq: int, nk: int, d: int, seed: int,
+             sigma=(1.0, 1.0, 1.0), mode: str = "normal") -> Fp8Inputs:
+    """Draw FP8 inputs q [batch, nq, hq, d], k and v [batch, nk, hkv, d].
+
+    ``mode="normal"``: ``rng.standard_normal(float32) * sigma`` for Q, K, V in
+    that order, each quantized with the per-tensor factor
+    descale = max|x| / 448 (the largest value maps to the largest e4m3
+    normal): codes = e4m3(x / descale).
+    ``mode="signs"``: Q and K rows hold 4 entries of +-1 at random positions
+    and zeros elsewhere (descale 1), so every score q.k is an integer in
+    [-4, 4]; V as in "normal".
+    """
+    rng = np.random.default_rng(seed)
+    qs, ks = (batch, nq, hq, d), (batch, nk, hkv, d)
+
+    def quant(x):
+        amax = float(np.abs(x).max()) if x.size else 0.0
+        ds = amax / 448.0 if amax > 0 else 1.0
+        return to_e4m3_bits(x / np.float32(ds)), ds
+
+    def signs(shape):
+        x = np.zeros(shape, dtype=np.float32)
+        flat = x.reshape(-1, shape[-1])
+        cols = np.argsort(rng.random(flat.shape), axis=1)[:, :4]
+        vals = np.where(rng.random((flat.shape[0], 4)) < 0.5, -1.0, 1.0).astype(np.float32)
+        np.put_along_axis(flat, cols, vals, axis=1)
+        return to_e4m3_bits(x), 1.0
+
+    if mode == "normal":
+        (qb, qd), (kb, kd) = (quant(rng.standard_normal(s, dtype=np.float32) * np.float32(sg))
+                              for s, sg in ((qs, sigma[0]), (ks, sigma[1])))
+    elif mode == "signs":
+        (qb, qd), (kb, kd) = signs(qs), signs(ks)
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    vb, vd = quant(rng.standard_normal(ks, dtype=np.float32) * np.float32(sigma[2]))
+    return Fp8Inputs(qb, kb, vb, qd, kd, vd)
