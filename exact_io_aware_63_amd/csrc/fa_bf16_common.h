@@ -1,6 +1,7 @@
-// Pieces shared by the bf16 kernels of libfa (forward and backward): vector
-// types, the 64-row tile of K, V, Q or dO as staged in LDS (16-byte units of
-// each row XOR-swizzled), its buffer-to-LDS loader, lane reductions and a
+// Pieces shared by the matrix-core kernels of libfa (bf16 forward and
+// backward, fp8 forward): vector types, the 64-row tile of K, V, Q or dO as
+// staged in LDS (16-byte units of each row XOR-swizzled), its buffer-to-LDS
+// loader, lane reductions, accumulator moves out of AGPRs and a
 // compile-time loop. Device code only; every definition has internal
 // linkage.
 #pragma once
@@ -65,6 +66,34 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Read an accumulator tile held in AGPRs into VGPRs (explicit moves, so
+// that the compiler keeps the tile itself in AGPRs).
+__device__ __forceinline__ f32x16 read_agpr(f32x16 a) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[i]));
+    r[i] = x;
+  }
+  return r;
+}
+
+// Multiply an accumulator tile that lives in AGPRs by a per-lane factor,
+// passing it through private memory: memory instructions take AGPR data
+// directly, so no vector instruction reads the tile and the compiler keeps
+// it in AGPRs everywhere else. Used only on the rare rescale path.
+__device__ __forceinline__ f32x16 scale_via_scratch(f32x16 a, float f) {
+  volatile f32x16 tmp;
+  tmp = a;
+  f32x16 x = tmp;
+  x *= f;
+  tmp = x;
+  f32x16 r = tmp;
+  asm volatile("" : "+a"(r));
+  return r;
 }
 
 // Start the loads of one 64-row tile of a bf16 tensor with rows of D values

@@ -81,34 +81,6 @@ __device__ __forceinline__ void mfma_result_guard() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Read an accumulator tile held in AGPRs into VGPRs (explicit moves, so
-// that the compiler keeps the tile itself in AGPRs).
-__device__ __forceinline__ f32x16 read_agpr(f32x16 a) {
-  f32x16 r;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float x;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[i]));
-    r[i] = x;
-  }
-  return r;
-}
-
-// Multiply an accumulator tile that lives in AGPRs by a per-lane factor,
-// passing it through private memory: memory instructions take AGPR data
-// directly, so no vector instruction reads the tile and the compiler keeps
-// it in AGPRs everywhere else. Used only on the rare rescale path.
-__device__ __forceinline__ f32x16 scale_via_scratch(f32x16 a, float f) {
-  volatile f32x16 tmp;
-  tmp = a;
-  f32x16 x = tmp;
-  x *= f;
-  tmp = x;
-  f32x16 r = tmp;
-  asm volatile("" : "+a"(r));
-  return r;
-}
-
 // Instruction plan of one key block for one wave (two 32-row query tiles).
 // The block has M matrix steps: 4*NC score MFMAs of the NEXT block (two
 // 32-key tiles x NC d-chunks x two query tiles) and 8*ND P V MFMAs of THIS

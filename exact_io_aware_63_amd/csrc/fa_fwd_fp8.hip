@@ -19,20 +19,27 @@
 //   * 64-key blocks of K (row-major, 16-byte units swizzled) and of V^T
 //     stream through LDS by buffer-to-LDS loads, double-buffered;
 //   * S^T = K Q^T: a lane holds 32 scores of one query row;
-//   * the weights 2^(x - m + kE), x = c s in base 2, are rounded to e4m3 and
-//     packed straight into the B operand of O^T += V^T P^T. Their byte order
+//   * the weights of a block are stored per row as ws = 2^(x - m - t + 8),
+//     x = c s in base 2, t = ceil(block max - m), so the block's largest
+//     weight lies in (2^7, 2^8]; they are rounded to e4m3 and packed straight
+//     into the B operand of O^T += V^T P^T, whose per-lane e8m0 scale
+//     (the row's 2^(t-8)) restores the true weights 2^(x - m) in the
+//     product. Their byte order
 //     (key tile kt, register r: key 32kt + 8(r/4) + 4*h2 + (r%4)) is what
 //     the V^T tiles are laid out for: a pre-pass (vt_pack_kernel) writes
 //     each 64-key block of V as a [128 d rows x 64 bytes] tile whose byte
 //     32*h2 + i of row d is V[key(h2, i)][d], so the A operand of a lane is
 //     32 contiguous bytes.
-// Weights: the reference m of a row is kept while the block maxima stay
-// below m + kRaise (2^(kE + kRaise) = 256 stays below the e4m3 maximum
-// 448); the offset kE = 6 puts the row maximum at 64, so weights down to
-// 2^-12 of it are e4m3 normals (3 mantissa bits).
+// Reference point: the first visible block of a row sets m; the block scale
+// absorbs any later growth of the maxima, so m moves again only when a
+// block maximum exceeds m + 64 (to keep the float32 sums far from
+// overflow), a rescale through private memory that realistic inputs never
+// reach. Stored weights down to 2^-14 of the block maximum are e4m3 normals
+// (3 mantissa bits).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <type_traits>
 
 #include "fa_bf16_common.h"
 #include "fa_launch.h"
@@ -47,8 +54,8 @@ constexpr int kBR8 = 256;                // query rows per workgroup
 constexpr int kBlk = 64;                 // keys per block
 constexpr int kVtRowBytes = kBlk;        // one V^T tile row: 64 keys of one d
 constexpr int kVtBytes = kD8 * kBlk;     // 8 KiB
-constexpr float kE = 6.f;                // weight exponent offset
-constexpr float kRaise8 = 2.f;           // lazy-reference headroom (base 2)
+constexpr float kRaiseFar = 64.f;        // a block maximum above m + 64 moves m
+constexpr int kTmin = -100;              // t is clamped to [-100, 64]: scale 2^(t-8)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kScaleOne = 127;           // e8m0 scale 2^0 of the scaled MFMA form
 
@@ -73,6 +80,38 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0,
                                                          kScaleOne);
 }
+
+// Score MFMAs (S^T tile = K operand x Q fragment) as inline asm, with the
+// Q fragment in AGPRs and the scores written to AGPRs. The compiler does
+// not see these as MFMAs, so it must never touch a score tile before the
+// result is written: the tile is an AGPR output that nothing reads until
+// read_agpr(), which follows mfma8_result_guard() at the end of the region
+// and moves the scores to VGPRs, where the next block's vector work reads
+// them.
+__device__ __forceinline__ f32x16 mfma8_qk_first(i32x8 a, i32x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "a"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma8_qk_acc(f32x16& d, i32x8 a, i32x8 b) {
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(d) : "v"(a), "a"(b));
+}
+// 32 wait states: more than a 16-pass MFMA result needs before a dependent
+// vector read.
+__device__ __forceinline__ void mfma8_result_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step plan of one block: 16 matrix steps. Steps 0..7: the score MFMAs of
+// the NEXT block, s -> key tile s/4, d chunk (s/2)%2, query tile s%2 (each
+// LDS operand serves both query tiles); steps 8..11: P V of query tile 0,
+// d tile s-8; steps 12..15: P V of query tile 1. The 16 groups of 4
+// weights (exp, e4m3 pack, row sum) of THIS block are spread over steps
+// 0..11: tile 0's group g at step g, tile 1's groups at steps 1, 3, 5, 7,
+// 8, 9, 10, 11, so each tile's P bytes are complete before its P V.
+constexpr int kQt1GroupStep[8] = {1, 3, 5, 7, 8, 9, 10, 11};
 
 // ---------------------------------------------------------------------------
 // V -> V^T tiles
@@ -219,6 +258,7 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
   if (nblk > 0) {
     issue_k8(kg, kstride, 0, Lk, kb[0], tid, w);
     issue_vt(vtg, vb[0], tid, w);
+    if (nblk > 1) issue_k8(kg, kstride, kBlk, Lk, kb[1], tid, w);
   }
 
   // A negative c is applied by flipping the sign bits of Q (exact in e4m3).
@@ -241,14 +281,19 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
       }
       qf[qt][cc] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      asm volatile("" : "+a"(qf[qt][cc]));  // only the matrix cores read Q: AGPRs
     }
   }
+  asm volatile("s_nop 4" ::: "memory");  // AGPR writes before the inline MFMAs read them
 
   f32x16 acc[2][4];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[qt][t] = f32x16{};
+    for (int t = 0; t < 4; ++t) {
+      acc[qt][t] = f32x16{};
+      asm volatile("" : "+a"(acc[qt][t]));  // the accumulators live in AGPRs
+    }
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
@@ -272,29 +317,56 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
-  for (int jb = 0; jb < nblk; ++jb) {
-    const int buf = jb & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block jb landed; every wave is done with block jb-1
-    if (jb + 1 < nblk) {
-      issue_k8(kg, kstride, (jb + 1) * kBlk, Lk, kb[buf ^ 1], tid, w);
-      issue_vt(vtg + static_cast<long>(jb + 1) * kVtBytes, vb[buf ^ 1], tid, w);
-    }
-    if (jb >= nblk_w) continue;
-    const int k0 = jb * kBlk;
-    const unsigned char* ks = kb[buf];
-    const unsigned char* vs = vb[buf];
-
-    // S^T = K Q^T: s[qt][kt][r] is key k0 + 32kt + 8(r/4) + 4*h2 + (r%4)
-    // against query wq0 + 32qt + j.
-    f32x16 s[2][2];
+  // S^T of one block from the K tile ks: s[qt][kt][r] is key
+  // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query wq0 + 32qt + j.
+  f32x16 s_ag[2][2];  // score MFMA outputs (AGPRs)
+  f32x16 sv[2][2];    // scores of the next block to process (VGPRs)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nblk_w > 0) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const i32x8 a0 = k_operand(ks, kt, 0);
-      const i32x8 a1 = k_operand(ks, kt, 1);
+      const i32x8 a0 = k_operand(kb[0], kt, 0);
+      const i32x8 a1 = k_operand(kb[0], kt, 1);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[qt][kt] = mfma8(a1, qf[qt][1], mfma8(a0, qf[qt][0], f32x16{}));
+      for (int qt = 0; qt < 2; ++qt) {
+        s_ag[qt][kt] = mfma8_qk_first(a0, qf[qt][0]);
+        mfma8_qk_acc(s_ag[qt][kt], a1, qf[qt][1]);
+      }
     }
+    mfma8_result_guard();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = read_agpr(s_ag[qt][kt]);
+  }
+
+  // One key block j; its scores sc are in registers and the loads of
+  // K_{j+1} and V^T_j are in flight (issued one block earlier).
+  //   head: wait for them; barrier (every wave is done with block j-1, so
+  //      the buffers of K_j and V^T_{j-1} are free); start the loads of
+  //      K_{j+2} and V^T_{j+1} into them;
+  //   body: mask, row maxima, reference; then one branch-free region in
+  //      which the matrix cores form the scores of block j+1 (sn) and
+  //      O^T += V^T_j P_j^T while the vector unit computes the weights of
+  //      block j: each score MFMA shares its slot with 14 vector
+  //      instructions of query tile 0, each P V MFMA of tile 0 with 28 of
+  //      tile 1 (sched_group_barrier fixes that interleave).
+  auto head = [&](auto par_tag, int jb) {
+    constexpr int PAR = decltype(par_tag)::value;  // jb & 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (jb + 2 < nblk) issue_k8(kg, kstride, (jb + 2) * kBlk, Lk, kb[PAR], tid, w);
+    if (jb + 1 < nblk)
+      issue_vt(vtg + static_cast<long>(jb + 1) * kVtBytes, vb[PAR ^ 1], tid, w);
+  };
+  auto body = [&](auto par_tag, int jb) {
+    constexpr int PAR = decltype(par_tag)::value;  // jb & 1
+    if (jb >= nblk_w) return;
+    const int k0 = jb * kBlk;
+    const unsigned char* k_next = kb[PAR ^ 1];  // K_{j+1}
+    const unsigned char* v_cur = vb[PAR];       // V^T_j
+    f32x16 (&sc)[2][2] = sv;  // this block's scores, read out by the previous region
     // Mask the blocks that reach past the keys or cross this wave's diagonal.
     if ((k0 + kBlk > Lk) || (CAUSAL && k0 + kBlk - 1 > wq0)) {
 #pragma unroll
@@ -305,21 +377,23 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            s[qt][kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? s[qt][kt][r] : -INFINITY;
+            sc[qt][kt][r] = (32 * kt + 8 * (r >> 2) + (r & 3) <= lim) ? sc[qt][kt][r] : -INFINITY;
       }
     }
     float mb[2];
     bool up = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float mx = fmaxf(s[qt][0][0], s[qt][1][0]);
+      float mx = fmaxf(sc[qt][0][0], sc[qt][1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[qt][0][r], s[qt][1][r]));
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[qt][0][r], sc[qt][1][r]));
       mb[qt] = xhalf_max(mx) * c;
       if (m_run[qt] == -INFINITY) m_run[qt] = mb[qt];
-      up = up || (mb[qt] > m_run[qt] + kRaise8);
+      up = up || (mb[qt] > m_run[qt] + kRaiseFar);
     }
     if (__any(up)) {  // wave-uniform, rare
+      // after the last P V MFMAs have written the accumulators
+      mfma8_result_guard();
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const float m_new = fmaxf(m_run[qt], mb[qt]);
@@ -327,39 +401,101 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
         m_run[qt] = m_new;
         l_run[qt] *= alpha;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[qt][t] *= alpha;
+        for (int t = 0; t < 4; ++t) acc[qt][t] = scale_via_scratch(acc[qt][t], alpha);
       }
+      asm volatile("s_nop 1" ::: "memory");  // AGPR writes before MFMA reads
     }
-    // weights 2^(c s - m + kE), rounded to e4m3 into the B operand bytes
-    // 16kt + r (row sums from the unrounded float32 weights)
+    // per-row block exponent t, exp offset 8 - m - t, B-operand scale byte
+    // 127 + (t - 8); a row with no visible key so far keeps t = 0 (its
+    // weights are all 0)
+    float off[2];
+    int tq[2], sbq[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const float off = (m_run[qt] == -INFINITY) ? 0.f : kE - m_run[qt];
-      float rs = 0.f;
-      int pw[8];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kt][4 * g + e], c, off));
-            rs += x[e];
-          }
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-          pw[4 * kt + g] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
-        }
-      l_run[qt] += rs;
-      const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[qt][t] = mfma8(v_operand(vs, t), pb, acc[qt][t]);
+      const bool none = m_run[qt] == -INFINITY;
+      tq[qt] = none ? 0 : static_cast<int>(ceilf(fmaxf(mb[qt] - m_run[qt], static_cast<float>(kTmin))));
+      off[qt] = (none ? 0.f : -m_run[qt]) + static_cast<float>(8 - tq[qt]);
+      sbq[qt] = kScaleOne + tq[qt] - 8;
     }
+
+    // The region (Plan above): LDS operands are read two steps before their
+    // first use; score operand p = 2kt + cc is first used at step 2p, value
+    // operand t (shared by both query tiles) at step 8 + t.
+    i32x8 kop[2][2], vop[4];
+    int pw[2][8];
+    float rs[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    auto loads_for = [&](auto S) {
+      constexpr int s = decltype(S)::value;
+      if constexpr (s < 8 && (s & 1) == 0) {
+        constexpr int pp = s / 2;
+        kop[pp >> 1][pp & 1] = k_operand(k_next, pp >> 1, pp & 1);
+      }
+      if constexpr (s >= 8 && s < 12) vop[s - 8] = v_operand(v_cur, s - 8);
+    };
+    // group g of query tile qt: score registers 4(g%4) .. +3 of key tile
+    // g/4, packed into B-operand word g
+    auto group = [&](int qt, int g) {
+      const int kt = g >> 2, r0 = 4 * (g & 3);
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][kt][r0 + e], c, off[qt]));
+      rs[qt][g & 1] += (x[0] + x[1]) + (x[2] + x[3]);
+      const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
+      pw[qt][g] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+    };
+    static_for<2>(loads_for);
+    static_for<16>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      if constexpr (s + 2 < 16) loads_for(std::integral_constant<int, s + 2>{});
+      if constexpr (s < 8) {
+        constexpr int kt = s >> 2, cc = (s >> 1) & 1, qt = s & 1;
+        if constexpr (cc == 0) s_ag[qt][kt] = mfma8_qk_first(kop[kt][0], qf[qt][0]);
+        else mfma8_qk_acc(s_ag[qt][kt], kop[kt][1], qf[qt][1]);
+      } else {
+        constexpr int qt = s >= 12 ? 1 : 0, tt = s - 8 - 4 * qt;
+        const i32x8 pb = {pw[qt][0], pw[qt][1], pw[qt][2], pw[qt][3],
+                          pw[qt][4], pw[qt][5], pw[qt][6], pw[qt][7]};
+        acc[qt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            vop[tt], pb, acc[qt][tt], 0, 0, 0, kScaleOne, 0, sbq[qt]);
+        asm volatile("" : "+a"(acc[qt][tt]));
+      }
+      if constexpr (s < 8) group(0, s);
+      static_for<8>([&](auto G) {
+        if constexpr (kQt1GroupStep[decltype(G)::value] == s) group(1, decltype(G)::value);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) l_run[qt] += ldexpf(rs[qt][0] + rs[qt][1], tq[qt] - 8);
+    // the next block's scores, after the score MFMAs of this region finished
+    mfma8_result_guard();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = read_agpr(s_ag[qt][kt]);
+  };
+
+  // Key loop, unrolled by two so every LDS address has a fixed buffer. A
+  // wave's last computed block also forms the scores of the block after it
+  // (from whatever the K buffer holds, discarded).
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  for (int jb = 0; jb < nblk; jb += 2) {
+    head(P0{}, jb);
+    body(P0{}, jb);
+    if (jb + 1 >= nblk) break;
+    head(P1{}, jb + 1);
+    body(P1{}, jb + 1);
   }
 
-  // Epilogue: o = dv * a / l, rounded once to bf16; LSE = ln 2 (m - kE + log2 l).
+  // Epilogue: o = dv * a / l, rounded once to bf16; LSE = ln 2 (m + log2 l).
+  mfma8_result_guard();  // the last P V MFMAs may still be in flight
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
+    f32x16 o_t[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o_t[t] = read_agpr(acc[qt][t]);
     const int qrow = wq0 + 32 * qt + j;
     const float l_tot = xhalf_sum(l_run[qt]);
     if (qrow < Lq) {
@@ -372,12 +508,12 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
         for (int g = 0; g < 4; ++g) {
           bf16x4 o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = static_cast<__bf16>(acc[qt][t][4 * g + e] * f);
+          for (int e = 0; e < 4; ++e) o4[e] = static_cast<__bf16>(o_t[t][4 * g + e] * f);
           *reinterpret_cast<bf16x4*>(og + 32 * t + 8 * g + 4 * h2) = o4;
         }
       if (h2 == 0)
         p.lse[(static_cast<long>(b) * p.hq + h) * Lq + qrow] =
-            l_tot > 0.f ? (m_run[qt] - kE + __log2f(l_tot)) * kLn2 : -INFINITY;
+            l_tot > 0.f ? (m_run[qt] + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }

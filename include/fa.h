@@ -249,7 +249,7 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O,
  * FlashAttention Pt 1: Personal Notes", contents, section 5.6). The cost
  * here is one rounding: the scores are exact products summed in float32;
  * the probabilities are rounded to e4m3 for the P V product (an absolute
- * error of at most 2^-4 P_ij, or 2^-16 of the row's largest weight when
+ * error of at most 2^-4 P_ij, or 2^-17 of the row's weight sum when
  * that is larger, per term); O is rounded once to bf16.
  *   Q [B, Nq, Hq, 128], K, V [B, Nk, Hkv, 128] : device, e4m3 bytes,
  *            16-byte aligned. Fixed length only; d must be 128.

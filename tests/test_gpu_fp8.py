@@ -4,10 +4,13 @@ the dequantized inputs.
 Tolerance, from the arithmetic of the kernel and of the fp8 matrix
 instruction:
 
-* P rounding. The normaliser l is the float32 sum of the unrounded weights
-  w = 2^(x - m + 6); each weight is rounded to e4m3 before the P V product:
-  at most 2^-4 w for a normal and 2^-10 (half the subnormal step) below
-  2^-6, while the row's largest weight, hence l, is at least 2^6.
+* P rounding. Each block stores a row's weights as ws = 2^(x - m - t + 8)
+  with t = ceil(block max - m), so the block's largest stored weight lies
+  in (2^7, 2^8]; the MFMA's per-lane operand scale 2^(t-8) restores the
+  true weights, and the normaliser l is the float32 sum of the unrounded
+  ones. Rounding ws to e4m3 costs at most 2^-4 ws for a normal and 2^-10
+  (half the subnormal step) below 2^-6, i.e. 2^(t-18) in true units, while
+  l exceeds the block's largest true weight 2^(t-1): at most 2^-17 of l.
 * Accumulation inside v_mfma_f32_32x32x64_f8f6f4. Its 64-product dot
   products are not exact: measured with one wave on the GPU (B = 1, rows of
   A with known sums), low bits of products next to a larger one in the same
@@ -23,7 +26,7 @@ With Pabs_i = sum_j P_ij |V_j| (the oracle's attention of |V|), Vsum_i =
 sum of |V_j| over the keys row i sees, and Sabs_ij = |scale| |q_i|.|k_j|
 (the absolute score sum), elementwise
 
-    |O_gpu - O_ref|_i <= 2^-4 Pabs_i + 2^-16 Vsum_i                  (P rounding)
+    |O_gpu - O_ref|_i <= 2^-4 Pabs_i + 2^-17 Vsum_i                  (P rounding)
                          + eps (1 + 2^-4) Pabs_i                      (P V sums)
                          + eps sum_j P_ij Sabs_ij (|V_j| + |O_i|)     (score sums)
                          + 2^-8 |O_ref|_i + 1e-6                      (bf16 O),
@@ -105,7 +108,7 @@ def _bounds(q, k, v, scale, causal, o_ref, lse_ref, exact):
             g = oracle.kv_head_of(h, hq, hkv)
             pabs, vsum, psv, ps = _row_terms(q[b, :, h], k[b, :, g], v[b, :, g], scale, causal,
                                              rows, o_ref[b, :, h])
-            round_p = 0.0 if exact else 2.0 ** -4 * pabs + 2.0 ** -16 * vsum
+            round_p = 0.0 if exact else 2.0 ** -4 * pabs + 2.0 ** -17 * vsum
             bo[b, :, h] = (round_p + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
                            2.0 ** -8 * np.abs(o_ref[b, :, h]) + 1e-6)
             bl[b, h] = EPS * ps + 1e-5 * (1 + np.abs(np.where(np.isfinite(lse_ref[b, h]),
@@ -215,7 +218,7 @@ def test_fp8_full_size_sampled():
         g = oracle.kv_head_of(int(h), w.hq, w.hkv)
         pabs, vsum, psv, ps = _row_terms(q[s, :, h], k[s, :, g], v[s, :, g], w.scale, True,
                                          np.array([i]), ro[n:n + 1])
-        bo[n] = (2.0 ** -4 * pabs + 2.0 ** -16 * vsum + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
+        bo[n] = (2.0 ** -4 * pabs + 2.0 ** -17 * vsum + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
                  2.0 ** -8 * np.abs(ro[n:n + 1]) + 1e-6)[0]
         bl[n] = EPS * ps[0] + 1e-5 * (1 + abs(rl[n]))
     go = o[0, picks[:, 2], picks[:, 1]].float().cpu().double().numpy()
