@@ -76,6 +76,12 @@ constexpr int kKRowBytes = kD8;
 constexpr int kKBytes = kBlk * kKRowBytes;
 __device__ __forceinline__ int k_swz8(int r) { return r & 7; }
 
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0,
                                                          kScaleOne);
@@ -90,11 +96,11 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
 // them.
 __device__ __forceinline__ f32x16 mfma8_qk_first(i32x8 a, i32x8 b) {
   f32x16 d;
-  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "a"(b));
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
   return d;
 }
 __device__ __forceinline__ void mfma8_qk_acc(f32x16& d, i32x8 a, i32x8 b) {
-  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(d) : "v"(a), "a"(b));
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 // 32 wait states: more than a 16-pass MFMA result needs before a dependent
 // vector read.
@@ -338,7 +344,7 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = read_agpr(s_ag[qt][kt]);
+      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = s_ag[qt][kt];
   }
 
   // One key block j; its scores sc are in registers and the loads of
@@ -384,10 +390,15 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
     bool up = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float mx = fmaxf(sc[qt][0][0], sc[qt][1][0]);
+      // two running maxima (shorter dependency chains), one v_max3 per two scores
+      float ma = fmaxf(sc[qt][0][0], sc[qt][1][0]);
+      float mc = fmaxf(sc[qt][0][1], sc[qt][1][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[qt][0][r], sc[qt][1][r]));
-      mb[qt] = xhalf_max(mx) * c;
+      for (int r = 2; r < 16; r += 2) {
+        ma = max3(ma, sc[qt][0][r], sc[qt][1][r]);
+        mc = max3(mc, sc[qt][0][r + 1], sc[qt][1][r + 1]);
+      }
+      mb[qt] = xhalf_max(fmaxf(ma, mc)) * c;
       if (m_run[qt] == -INFINITY) m_run[qt] = mb[qt];
       up = up || (mb[qt] > m_run[qt] + kRaiseFar);
     }
@@ -473,7 +484,7 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = read_agpr(s_ag[qt][kt]);
+      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = s_ag[qt][kt];
   };
 
   // Key loop, unrolled by two so every LDS address has a fixed buffer. A
