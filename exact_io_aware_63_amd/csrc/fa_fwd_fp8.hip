@@ -65,16 +65,18 @@ __host__ __device__ constexpr int key_of_byte(int h2, int i) {
   return 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h2 + (i & 3);
 }
 
-// Physical 16-byte unit of logical unit u in V^T tile row d: consecutive
-// rows of a 128-byte bank cycle spread over all units.
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 3; }
+// LDS swizzles. A ds_read_b128 serves 16 lanes per pass from one 256-byte
+// bank window, so the 16 rows read by 16 consecutive lanes (same logical
+// unit) must fall on 16 different 16-byte bank groups.
+// V^T tile rows are 64 bytes: row d sits at bank groups 4(d%4) .. +3, and
+// logical unit u is stored at unit u ^ ((d / 4) % 4).
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 2) & 3; }
 
-// K tile: 64 keys x 128 bytes, logical 16-byte unit u of row r stored at
-// unit u ^ (r & 7), so the 8 rows read by 8 consecutive lanes (same logical
-// unit) fall on 8 different units.
+// K tile: 64 keys x 128 bytes; row r sits at bank groups 8(r%2) .. +7, and
+// logical unit u is stored at unit u ^ ((r / 2) % 8).
 constexpr int kKRowBytes = kD8;
 constexpr int kKBytes = kBlk * kKRowBytes;
-__device__ __forceinline__ int k_swz8(int r) { return r & 7; }
+__device__ __forceinline__ int k_swz8(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
