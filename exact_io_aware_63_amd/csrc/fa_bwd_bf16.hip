@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <type_traits>
 
 #include "fa_bf16_common.h"
 #include "fa_launch.h"
@@ -330,27 +331,38 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qs, r0, cc, lane), kf[cc], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ds_, r0, cc, lane), vf[cc], dp, 0, 0, 0);
       }
-      // P = 2^(c s - LSE log2 e) on visible pairs, dS = P (dP - D)
+      // P = 2^(c s - LSE log2 e) on visible pairs, dS = P (dP - D). A
+      // sub-block whose pairs all exist and are visible (wave-uniform; most
+      // of them under the causal mask) skips the per-element test.
       f32x16 pr, dsr;
+      auto probs = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rr = r0 + 8 * g4 + 4 * h2;
-        const float4 l4 = *reinterpret_cast<const float4*>(&lse_st[buf][rr]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&d_st[buf][rr]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int rr = r0 + 8 * g4 + 4 * h2;
+          const float4 l4 = *reinterpret_cast<const float4*>(&lse_st[buf][rr]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&d_st[buf][rr]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          const int q = qs0 + mrow(r, h2);
-          const bool vis = visible<CAUSAL, WIN>(p, q, key, sb.Lq, sb.Lk);
-          float off = neg_lse2<BIAS>(lv[e]);
-          if constexpr (BIAS) off = __builtin_fmaf(bf16_bits_to_float(bias_v[r]), kLog2e, off);
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, off));
-          pr[r] = vis ? pe : 0.f;
-          dsr[r] = pr[r] * (dp[r] - dvv[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float off = neg_lse2<BIAS>(lv[e]);
+            if constexpr (BIAS) off = __builtin_fmaf(bf16_bits_to_float(bias_v[r]), kLog2e, off);
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, off));
+            if constexpr (MASKED) {
+              const int q = qs0 + mrow(r, h2);
+              pr[r] = visible<CAUSAL, WIN>(p, q, key, sb.Lq, sb.Lk) ? pe : 0.f;
+            } else {
+              pr[r] = pe;
+            }
+            dsr[r] = pr[r] * (dp[r] - dvv[e]);
+          }
         }
-      }
+      };
+      const bool full = !WIN && qs0 + 31 < sb.Lq && kw0 + 31 < sb.Lk && (!CAUSAL || qs0 >= kw0 + 31);
+      if (full) probs(std::false_type{});
+      else probs(std::true_type{});
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries (two 16-chunks)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -504,19 +516,29 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vs, r0, cc, lane), dof[cc], dpt, 0, 0, 0);
       }
       f32x16 dst;
+      auto dscores = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = ks0 + mrow(r, h2);
-        const bool vis = visible<CAUSAL, WIN>(p, qrow, kk, sb.Lq, sb.Lk);
-        float off = nlse2;
-        if constexpr (BIAS) {
-          const uint32_t wd = bias_v[r >> 2][(r >> 1) & 1];
-          off = __builtin_fmaf(__uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16)), kLog2e,
-                               off);
+        for (int r = 0; r < 16; ++r) {
+          float off = nlse2;
+          if constexpr (BIAS) {
+            const uint32_t wd = bias_v[r >> 2][(r >> 1) & 1];
+            off = __builtin_fmaf(__uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16)),
+                                 kLog2e, off);
+          }
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, off));
+          if constexpr (MASKED) {
+            const int kk = ks0 + mrow(r, h2);
+            dst[r] = visible<CAUSAL, WIN>(p, qrow, kk, sb.Lq, sb.Lk) ? pe * (dpt[r] - drow) : 0.f;
+          } else {
+            dst[r] = pe * (dpt[r] - drow);
+          }
         }
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, off));
-        dst[r] = vis ? pe * (dpt[r] - drow) : 0.f;
-      }
+      };
+      // all pairs of the sub-block exist and are visible: no per-element test
+      const bool full = !WIN && ks0 + 31 < sb.Lk && wq0 + 31 < sb.Lq && (!CAUSAL || ks0 + 31 <= wq0);
+      if (full) dscores(std::false_type{});
+      else dscores(std::true_type{});
       // dQ^T += K^T dS^T over the 32 keys (two 16-chunks)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
