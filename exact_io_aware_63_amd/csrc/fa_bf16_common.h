@@ -68,6 +68,27 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Score MFMA (S^T tile = K operand x Q fragment), written as inline asm so
+// that the score accumulator is a VGPR (the vector unit reads it next) while
+// the Q fragment stays in an AGPR (only the matrix cores read it). The
+// compiler does not see these as MFMAs: the dependent vector reads of a
+// score tile are kept at least 19 wait states after its last MFMA by the
+// instruction plan and by explicit s_nop guards.
+__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// 21 wait states: covers a 16-pass MFMA result before a dependent read.
+__device__ __forceinline__ void mfma_result_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Read an accumulator tile held in AGPRs into VGPRs (explicit moves, so
 // that the compiler keeps the tile itself in AGPRs).
 __device__ __forceinline__ f32x16 read_agpr(f32x16 a) {

@@ -255,10 +255,15 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
     }
     kf[cc] = as_bf16x8(a);
     vf[cc] = as_bf16x8(c);
+    asm volatile("" : "+a"(kf[cc]), "+a"(vf[cc]));  // only the matrix cores read them: AGPRs
   }
+  asm volatile("s_nop 4" ::: "memory");  // AGPR writes before the inline MFMAs read them
   f32x16 dk[ND], dv[ND];
 #pragma unroll
-  for (int t = 0; t < ND; ++t) dk[t] = dv[t] = f32x16{};
+  for (int t = 0; t < ND; ++t) {
+    dk[t] = dv[t] = f32x16{};
+    asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));  // the accumulators live in AGPRs
+  }
 
   // Query blocks: every q-head of the group, rows from the block that holds
   // key k0 (causal) or from 0, to the end of the sequence; with a window,
@@ -325,12 +330,16 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
           bias_v[r] = bgh[static_cast<long>(min(qs0 + mrow(r, h2), sb.Lq - 1)) * p.bias_sr];
       }
       // S = Q K^T and dP = dO V^T: lane = key, register r = query qs0 + mrow(r)
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // (inline-asm MFMAs: results in VGPRs for the vector work that follows,
+      // read only after mfma_result_guard())
+      f32x16 s = mfma_qk_first(row_operand<D>(qs, r0, 0, lane), kf[0]);
+      f32x16 dp = mfma_qk_first(row_operand<D>(ds_, r0, 0, lane), vf[0]);
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qs, r0, cc, lane), kf[cc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ds_, r0, cc, lane), vf[cc], dp, 0, 0, 0);
+      for (int cc = 1; cc < NC; ++cc) {
+        mfma_qk_acc(s, row_operand<D>(qs, r0, cc, lane), kf[cc]);
+        mfma_qk_acc(dp, row_operand<D>(ds_, r0, cc, lane), vf[cc]);
       }
+      mfma_result_guard();
       // P = 2^(c s - LSE log2 e) on visible pairs, dS = P (dP - D). A
       // sub-block whose pairs all exist and are visible (wave-uniform; most
       // of them under the causal mask) skips the per-element test.
@@ -372,6 +381,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
         for (int t = 0; t < ND; ++t) {
           dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ds_, r0, t, g, lane), pb, dv[t], 0, 0, 0);
           dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, r0, t, g, lane), sbv, dk[t], 0, 0, 0);
+          asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
         }
       }
     }
@@ -379,6 +389,13 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
 
   // dK = scale (dK^T)^T, dV = (dV^T)^T: lane = key, register r of d-tile t =
   // d column 32t + mrow(r); four consecutive d values per 8-byte store.
+  // Explicit reads out of the AGPRs, after the last MFMAs have written them.
+  mfma_result_guard();
+#pragma unroll
+  for (int t = 0; t < ND; ++t) {
+    dk[t] = read_agpr(dk[t]);
+    dv[t] = read_agpr(dv[t]);
+  }
   if (key < sb.Lk) {
     u16* dkg = static_cast<u16*>(p.dk) + (sb.k_tok0 + key) * kstride + static_cast<long>(kvh) * D;
     u16* dvg = static_cast<u16*>(p.dv) + (sb.k_tok0 + key) * kstride + static_cast<long>(kvh) * D;
@@ -450,7 +467,9 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
     }
     qf[cc] = as_bf16x8(a);
     dof[cc] = as_bf16x8(c);
+    asm volatile("" : "+a"(qf[cc]), "+a"(dof[cc]));  // only the matrix cores read them: AGPRs
   }
+  asm volatile("s_nop 4" ::: "memory");  // AGPR writes before the inline MFMAs read them
   const RowIndex ri = row_index(p, sb, b, h);
   const float nlse2 = qrow < sb.Lq ? neg_lse2<BIAS>(p.lse[ri.at(qrow)]) : 0.f;
   // this lane's bias row (clamped into the sequence), 4 * h2 keys in: a run
@@ -464,7 +483,10 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
 
   f32x16 dq[ND];
 #pragma unroll
-  for (int t = 0; t < ND; ++t) dq[t] = f32x16{};
+  for (int t = 0; t < ND; ++t) {
+    dq[t] = f32x16{};
+    asm volatile("" : "+a"(dq[t]));  // the accumulators live in AGPRs
+  }
 
   // Key blocks: from 0 (or, with a window, the block holding the first
   // row's window start) to the last key any row of the tile sees.
@@ -509,12 +531,15 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
           bias_v[g] = *reinterpret_cast<const u32x2*>(brow + min(ks0 + 8 * g, kmax));
       }
       // S^T = K Q^T and dP^T = V dO^T: lane = query, register r = key ks0 + mrow(r)
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      // (inline-asm MFMAs: results in VGPRs, read only after mfma_result_guard())
+      f32x16 st = mfma_qk_first(row_operand<D>(ks, r0, 0, lane), qf[0]);
+      f32x16 dpt = mfma_qk_first(row_operand<D>(vs, r0, 0, lane), dof[0]);
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ks, r0, cc, lane), qf[cc], st, 0, 0, 0);
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vs, r0, cc, lane), dof[cc], dpt, 0, 0, 0);
+      for (int cc = 1; cc < NC; ++cc) {
+        mfma_qk_acc(st, row_operand<D>(ks, r0, cc, lane), qf[cc]);
+        mfma_qk_acc(dpt, row_operand<D>(vs, r0, cc, lane), dof[cc]);
       }
+      mfma_result_guard();
       f32x16 dst;
       auto dscores = [&](auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -545,13 +570,19 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
         const bf16x8 sbv = pack_chunk(dst, g);
 #pragma unroll
         for (int t = 0; t < ND; ++t)
+        {
           dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, r0, t, g, lane), sbv, dq[t], 0, 0, 0);
+          asm volatile("" : "+a"(dq[t]));
+        }
       }
     }
   }
 
   // dQ = scale (dQ^T)^T: lane = query, register r of d-tile t = d column
-  // 32t + mrow(r).
+  // 32t + mrow(r); explicit reads out of the AGPRs after the last MFMAs.
+  mfma_result_guard();
+#pragma unroll
+  for (int t = 0; t < ND; ++t) dq[t] = read_agpr(dq[t]);
   if (qrow < sb.Lq) {
     u16* dqg = static_cast<u16*>(p.dq) + (sb.q_tok0 + qrow) * qstride + static_cast<long>(h) * D;
 #pragma unroll

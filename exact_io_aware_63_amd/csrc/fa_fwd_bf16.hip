@@ -60,27 +60,6 @@ constexpr int kBC = kTileRows;      // keys per K/V block
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRaise = 16.f;      // the main loop keeps m while the block max is <= m + 16
 
-// Score MFMA (S^T tile = K operand x Q fragment), written as inline asm so
-// that the score accumulator is a VGPR (the vector unit reads it next) while
-// the Q fragment stays in an AGPR (only the matrix cores read it). The
-// compiler does not see these as MFMAs: the dependent vector reads of a
-// score tile are kept at least 19 wait states after its last MFMA by the
-// instruction plan and by explicit s_nop guards.
-__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
-  f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma_qk_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-// 21 wait states: covers a 16-pass MFMA result before a dependent read.
-__device__ __forceinline__ void mfma_result_guard() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Instruction plan of one key block for one wave (two 32-row query tiles).
 // The block has M matrix steps: 4*NC score MFMAs of the NEXT block (two
 // 32-key tiles x NC d-chunks x two query tiles) and 8*ND P V MFMAs of THIS
