@@ -204,27 +204,33 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None, bias_block=None):
 # Shader clock under load
 # ---------------------------------------------------------------------------
 
-def sclk_under_load(step, sync, launch_ms: float, seconds: float = 1.5):
+def sclk_under_load(step, sync, launch_ms: float, max_seconds: float = 30.0):
     """Mean GFX clock (MHz) over the XCDs, read with ``amd-smi metric --clock``
-    while about ``seconds`` of back-to-back launches run; None without amd-smi."""
+    while launches keep the GPU busy for the whole life of the amd-smi process
+    (its own start-up takes a second or more, so a fixed burst of launches can
+    end before it reads); None without amd-smi or if it does not answer."""
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
     out = {}
 
     def sample():
-        time.sleep(min(0.4, seconds / 3))
         try:
             out["text"] = subprocess.run([exe, "metric", "-g", "0", "--clock"], capture_output=True,
-                                         text=True, timeout=30).stdout
+                                         text=True, timeout=max_seconds).stdout
         except Exception:  # pragma: no cover - tool failure leaves the figure empty
             out["text"] = ""
 
-    n = max(1, int(seconds / max(launch_ms * 1e-3, 1e-6)))
+    chunk = max(1, int(0.05 / max(launch_ms * 1e-3, 1e-6)))  # about 50 ms of launches
+    for _ in range(chunk):  # the GPU is already busy when the tool starts
+        step()
     th = threading.Thread(target=sample)
     th.start()
-    for _ in range(n):
-        step()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < max_seconds:
+        for _ in range(chunk):
+            step()
+        sync()
     sync()
     th.join()
     clocks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out.get("text", ""))]
