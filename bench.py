@@ -204,6 +204,9 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None, bias_block=None):
 # Shader clock under load
 # ---------------------------------------------------------------------------
 
+MIN_PLAUSIBLE_SCLK_MHZ = 1000
+
+
 def sclk_under_load(step, sync, launch_ms: float, max_seconds: float = 30.0):
     """Mean GFX clock (MHz) over the XCDs, read with ``amd-smi metric --clock``
     while launches keep the GPU busy for the whole life of the amd-smi process
@@ -234,8 +237,17 @@ def sclk_under_load(step, sync, launch_ms: float, max_seconds: float = 30.0):
     sync()
     th.join()
     clocks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out.get("text", ""))]
-    return {"mean": float(np.mean(clocks)), "min": min(clocks), "max": max(clocks),
-            "xcds": len(clocks)} if clocks else None
+    if not clocks:
+        return None
+    rec = {"mean": float(np.mean(clocks)), "min": min(clocks), "max": max(clocks),
+           "xcds": len(clocks)}
+    if rec["mean"] < MIN_PLAUSIBLE_SCLK_MHZ:
+        # A matrix-core-bound launch does not run below 1 GHz: such a figure is
+        # not the shader clock under this load (some boxes report an idle or
+        # averaged value), so it is kept for the record and not used.
+        rec = {"mean": None, "reported_mean": rec["mean"], "xcds": rec["xcds"],
+               "rejected": f"below {MIN_PLAUSIBLE_SCLK_MHZ} MHz under load"}
+    return rec
 
 
 # ---------------------------------------------------------------------------
@@ -602,7 +614,7 @@ def main(argv=None):
         "pct_of_mfma_peak_at_measured_sclk": (
             100.0 * value / ((PEAK_FP8_TFLOPS if fp8_x is not None else PEAK_BF16_TFLOPS)
                              * sclk["mean"] / 2400.0)
-            if (w.dtype == "bf16" and sclk) else None),
+            if (w.dtype == "bf16" and sclk and sclk.get("mean")) else None),
         "detail": {
             "alg_flops": flops,
             "alg_hbm_bytes": abytes,
