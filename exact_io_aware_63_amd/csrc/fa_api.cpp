@@ -37,11 +37,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 struct DeviceCheck {
   std::once_flag once;
   int status = FA_OK;
+  int cus = 0;  // compute units, for the choice of launch shape
   char msg[256] = "";
 };
 DeviceCheck g_devices[kMaxDevices];
 
-int check_device() {
+int check_device(int* cus = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess)
@@ -57,6 +58,7 @@ int check_device() {
       snprintf(dc.msg, sizeof(dc.msg), "hipGetDeviceProperties failed: %s", hipGetErrorString(pe));
       return;
     }
+    dc.cus = prop.multiProcessorCount;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
       dc.status = FA_ERR_UNSUPPORTED;
       snprintf(dc.msg, sizeof(dc.msg), "device %d is %s; libfa is built for gfx950 only", dev,
@@ -64,6 +66,7 @@ int check_device() {
     }
   });
   if (dc.status != FA_OK) return fail(dc.status, "%s", dc.msg);
+  if (cus != nullptr) *cus = dc.cus;
   return FA_OK;
 }
 
@@ -134,9 +137,11 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   int st = validate(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, cu_seqlens, tile_rows, &noop);
   if (st != FA_OK || noop) return st;
   if (bias != nullptr && (st = validate_bias(*bias, Nk)) != FA_OK) return st;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != FA_OK) return st;
   fa::FwdParams p;
+  p.num_cus = cus;
   p.q = Q;
   p.k = K;
   p.v = V;

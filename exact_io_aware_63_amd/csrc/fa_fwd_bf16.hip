@@ -121,23 +121,35 @@ static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
 // score registers (runs of 4 consecutive keys, 8 bytes) straight into
 // registers, one block ahead; scores then carry t = scale * s + b in
 // natural units and the base-2 factor becomes log2(e).
-template <int D, bool CAUSAL, bool WIN, bool BIAS>
+// SPLIT (no mask but the key count, no window, no bias): for grids that
+// would leave compute units idle, a workgroup owns 128 query rows and its
+// two wave pairs take the first and the second half of the key blocks;
+// at the end the second pair hands its (m, l, a) to the first through LDS,
+// which merges them by the rule for two blocks of "Carry the Normalizer"
+// (common reference m = max(m1, m2), each part scaled by e^(m_i - m)).
+template <int D, bool CAUSAL, bool WIN, bool BIAS, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_kernel(FwdParams p, int n_qt) {
+  static_assert(!SPLIT || (!CAUSAL && !WIN && !BIAS), "key halves only for the plain mask");
   using T = Tile<D>;
   using PL = Plan<D>;
   constexpr int NC = D / 16;  // 16-wide d chunks of the QK^T contraction
   constexpr int ND = D / 32;  // 32-row tiles of O^T
+  constexpr int NH = SPLIT ? 2 : 1;               // key ranges per workgroup
+  constexpr int ROWS = SPLIT ? kBR / 2 : kBR;     // query rows per workgroup
   // K runs one block ahead of V: block j+1's scores are formed while block
-  // j's probabilities meet V, so each tensor has its own two buffers.
-  __shared__ __attribute__((aligned(1024))) unsigned char kb0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char kb1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char vb0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char vb1[T::kBytes];
+  // j's probabilities meet V, so each tensor has its own two buffers (one
+  // per key half with SPLIT).
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[NH * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[NH * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[NH * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[NH * T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = SPLIT ? (w >> 1) : 0;   // key half of this wave
+  const int wrow = SPLIT ? (w & 1) : w;    // 64-row group of this wave
   const int j = lane & 31;   // query column of S^T / O^T; key row of the K operand
   const int h2 = lane >> 5;  // half-wave
 
@@ -185,7 +197,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     k_tok0 = static_cast<long>(b) * p.nk;
     lse_base = (static_cast<long>(b) * p.hq + h) * p.nq;
   }
-  const int q0 = tile * kBR;
+  const int q0 = tile * ROWS;
   if (q0 >= Lq) return;
 
   const long qstride = static_cast<long>(p.hq) * D;
@@ -199,28 +211,51 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // all lie past the end of the queries computes nothing (it still loads
   // its share of every tile and meets every barrier).
   int kend = Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBR, Lq));
+  if (CAUSAL) kend = min(kend, min(q0 + ROWS, Lq));
   int kb_base = 0;  // first key block of the workgroup
   if constexpr (WIN) {
     if (p.win_right >= 0) kend = min(kend, min(q0 + kBR, Lq) - 1 + p.win_right + 1);
     if (p.win_left >= 0) kb_base = max(0, q0 - p.win_left) / kBC;
   }
-  const int key_base = kb_base * kBC;  // first key of local block 0
   int nblk;
-  if constexpr (WIN) nblk = kend > key_base ? (kend + kBC - 1) / kBC - kb_base : 0;
+  if constexpr (WIN) nblk = kend > kb_base * kBC ? (kend + kBC - 1) / kBC - kb_base : 0;
   else nblk = (kend + kBC - 1) / kBC;
-  const int wq0 = q0 + 64 * w;  // first query row of this wave
-  int nblk_w = wq0 >= Lq ? 0 : nblk;
+  // With SPLIT, half h streams blocks h*nh0 .. of the nblk (nh0 of them for
+  // half 0, the rest for half 1); the loop runs nh0 steps for both.
+  int nbh[NH];
+  if constexpr (SPLIT) {
+    const int nh0 = (nblk + 1) / 2;
+    nbh[0] = nh0;
+    nbh[1] = nblk - nh0;
+    kb_base = half * nh0;
+    nblk = nh0;
+  } else {
+    nbh[0] = nblk;
+  }
+  const int key_base = kb_base * kBC;  // first key of local block 0 (of this wave's half)
+  const int wq0 = q0 + 64 * wrow;      // first query row of this wave
+  int nblk_w = wq0 >= Lq ? 0 : (SPLIT ? nbh[half] : nblk);
   if (CAUSAL) nblk_w = min(nblk_w, wq0 / kBC + 1 - kb_base);
   if constexpr (WIN) {
     if (p.win_right >= 0) nblk_w = min(nblk_w, (wq0 + 63 + p.win_right) / kBC + 1 - kb_base);
   }
 
-  if (nblk > 0) {
-    issue_tile<D>(kg, kstride, key_base, Lk, kb0, tid, w);
-    issue_tile<D>(vg, kstride, key_base, Lk, vb0, tid, w);
-    if (nblk > 1) issue_tile<D>(kg, kstride, key_base + kBC, Lk, kb1, tid, w);
+  // Every tile is loaded by all four waves; hk(h) is the first key of
+  // half h, and a half streams nbh[h] blocks.
+  auto hk = [&](int h) { return SPLIT ? h * nblk * kBC : key_base; };
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    if (nbh[h] > 0) {
+      issue_tile<D>(kg, kstride, hk(h), Lk, kb0 + h * T::kBytes, tid, w);
+      issue_tile<D>(vg, kstride, hk(h), Lk, vb0 + h * T::kBytes, tid, w);
+      if (nbh[h] > 1) issue_tile<D>(kg, kstride, hk(h) + kBC, Lk, kb1 + h * T::kBytes, tid, w);
+    }
   }
+  // this wave's view of the buffers (its key half)
+  unsigned char* const kw0 = kb0 + half * T::kBytes;
+  unsigned char* const kw1 = kb1 + half * T::kBytes;
+  unsigned char* const vw0 = vb0 + half * T::kBytes;
+  unsigned char* const vw1 = vb1 + half * T::kBytes;
 
   // A negative scale is applied by negating Q (exact in bf16), so that the
   // base-2 factor c below is >= 0 and max(c*s) = c*max(s). With a bias the
@@ -339,7 +374,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = k_operand(kb0, kt, cc);
+        const bf16x8 a = k_operand(kw0, kt, cc);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           if (cc == 0) sa[qt][kt] = mfma_qk_first(a, qf[qt][cc]);
@@ -365,13 +400,18 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     unsigned char* v_free = PAR ? vb0 : vb1;        // V_{j-1}, consumed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (jb + 2 < nblk) issue_tile<D>(kg, kstride, key_base + (jb + 2) * kBC, Lk, k_free, tid, w);
-    if (jb + 1 < nblk) issue_tile<D>(vg, kstride, key_base + (jb + 1) * kBC, Lk, v_free, tid, w);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      if (jb + 2 < nbh[h])
+        issue_tile<D>(kg, kstride, hk(h) + (jb + 2) * kBC, Lk, k_free + h * T::kBytes, tid, w);
+      if (jb + 1 < nbh[h])
+        issue_tile<D>(vg, kstride, hk(h) + (jb + 1) * kBC, Lk, v_free + h * T::kBytes, tid, w);
+    }
   };
   auto body = [&](auto par_tag, int jb, f32x16(&sc)[2][2], f32x16(&sn)[2][2]) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
-    const unsigned char* k_next = PAR ? kb0 : kb1;  // K_{j+1}
-    const unsigned char* v_cur = PAR ? vb1 : vb0;   // V_j
+    const unsigned char* k_next = PAR ? kw0 : kw1;  // K_{j+1}
+    const unsigned char* v_cur = PAR ? vw1 : vw0;   // V_j
     if (jb >= nblk_w) return;
     const int k0 = key_base + jb * kBC;
     mfma_result_guard();  // the last score MFMAs of sc may still be in flight
@@ -537,11 +577,49 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
 
   // Epilogue: o = a / l, rounded once to bf16; LSE = ln(2) * (m + log2 l).
   mfma_result_guard();  // the last P V MFMAs may still be in flight
+  // SPLIT: the second key half's (m, l, a) of each lane, staged in the
+  // (now free) K and V buffers of the wave pair's row group.
+  const float* xa = reinterpret_cast<const float*>(wrow ? kb1 : kb0);  // 2*ND*16 per lane
+  const float* xm = reinterpret_cast<const float*>(wrow ? vb1 : vb0);  // m, l per query tile
+  if constexpr (SPLIT) {
+    __syncthreads();  // every wave is done with the K/V buffers
+    if (half == 1) {
+      float* ya = reinterpret_cast<float*>(wrow ? kb1 : kb0);
+      float* ym = reinterpret_cast<float*>(wrow ? vb1 : vb0);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          const f32x16 a = read_agpr(acc[qt][t]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ya[((qt * ND + t) * 16 + r) * 64 + lane] = a[r];
+        }
+        ym[qt * 64 + lane] = m_run[qt];
+        ym[(2 + qt) * 64 + lane] = l_run[qt];
+      }
+    }
+    __syncthreads();
+    if (half == 1) return;
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     f32x16 o_t[ND];
 #pragma unroll
     for (int t = 0; t < ND; ++t) o_t[t] = read_agpr(acc[qt][t]);
+    if constexpr (SPLIT) {  // both parts to the common reference max(m0, m1)
+      const float m0 = m_run[qt];
+      const float m1 = xm[qt * 64 + lane];
+      const float mm = fmaxf(m0, m1);
+      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+      l_run[qt] = l_run[qt] * a0 + xm[(2 + qt) * 64 + lane] * a1;
+      m_run[qt] = mm;
+#pragma unroll
+      for (int t = 0; t < ND; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o_t[t][r] = o_t[t][r] * a0 + xa[((qt * ND + t) * 16 + r) * 64 + lane] * a1;
+    }
     const int qrow = wq0 + 32 * qt + j;
     const float l_tot = xhalf_sum(l_run[qt]);
     if (qrow < Lq) {
@@ -571,15 +649,27 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int n_qt = (p.nq + kBR - 1) / kBR;
   const unsigned grid = static_cast<unsigned>(n_qt) * p.hq * p.batch;
+  const bool plain = p.bias == nullptr && p.win_left < 0 && p.win_right < 0;
+  if constexpr (!CAUSAL) {
+    // A grid of 256-row tiles that leaves compute units idle: 128-row
+    // workgroups whose wave pairs split the keys, twice as many of them.
+    if (plain && grid <= static_cast<unsigned>(p.num_cus)) {
+      const int n_qt2 = (p.nq + kBR / 2 - 1) / (kBR / 2);
+      const unsigned grid2 = static_cast<unsigned>(n_qt2) * p.hq * p.batch;
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true>), dim3(grid2),
+                         dim3(kThreads), 0, stream, p, n_qt2);
+      return hipGetLastError();
+    }
+  }
   if (p.bias != nullptr)  // the host never combines a bias with a window
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, p, n_qt);
-  else if (p.win_left >= 0 || p.win_right >= 0)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, p, n_qt);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, p, n_qt);
+  else if (!plain)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, p, n_qt);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, p, n_qt);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, p, n_qt);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ struct FwdParams {
   long bias_sb;               //   element (s, h, i, j) at bias[s*sb + h*sh + i*sr + j]
   long bias_sh;
   long bias_sr;
+  int num_cus;                // compute units of the device (choice of launch shape)
 };
 
 // Launch the bf16 kernel for head width D (64 or 128), causal or not.

@@ -49,6 +49,16 @@ SMALL = [
     ("bf16", 3, 66, 3, 700, 700, 64, True, None),
     ("bf16", 1, 32, 8, 0, 0, 128, True, [1000, 37, 513, 256, 700, 1, 0, 300]),
     ("bf16", 1, 32, 8, 0, 0, 64, True, [900, 5, 512, 257, 0, 640, 129, 1]),
+    # Non-causal grids of 256-row tiles that fit on the compute units at once
+    # (all the cases above) run 128-row workgroups whose wave pairs split the
+    # key blocks in two halves; the edges of that split:
+    ("bf16", 1, 4, 2, 129, 65, 128, False, None),   # two key blocks, one per half, ragged
+    ("bf16", 1, 4, 2, 130, 1, 64, False, None),     # one key: the second half has no block
+    ("bf16", 1, 2, 2, 260, 320, 64, False, None),   # five blocks: halves of three and two
+    ("bf16", 1, 2, 1, 100, 193, 128, False, None),  # last block holds one key
+    # more 256-row tiles than compute units (320 on a 256-CU part): no key split
+    ("bf16", 1, 64, 8, 1100, 1100, 128, False, None),
+    ("bf16", 2, 40, 5, 900, 900, 64, False, None),
     ("fp32", 2, 4, 2, 300, 300, 128, True, None),
     ("fp32", 1, 4, 1, 200, 333, 64, False, None),
     ("fp32", 1, 2, 1, 333, 200, 128, True, None),
