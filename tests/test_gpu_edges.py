@@ -188,18 +188,20 @@ def test_empty_keys_give_zero_and_neg_inf():
     import torch
     say("[case] Nk = 0 and empty packed sequences")
     fa = _fa()
+    # non-causal bf16 takes the key-halves schedule at this size: both halves
+    # are empty and the merge must still give O = 0, LSE = -inf
     for dtype in (torch.bfloat16, torch.float32):
-        q = torch.randn(2, 70, 4, 64, device="cuda").to(dtype)
-        k = torch.empty(2, 0, 2, 64, device="cuda", dtype=dtype)
-        o = torch.full_like(q, 7.0)
-        lse = torch.zeros(2, 4, 70, device="cuda")
-        # Nk = 0 still needs valid (non-NULL) pointers: pass q's storage.
-        st = (fa.fa_fwd if dtype == torch.bfloat16 else fa.fa_fwd_fp32)(
-            q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            2, 4, 2, 70, 0, 64, 0.125, 1, None, torch.cuda.current_stream().cuda_stream)
-        torch.cuda.synchronize()
-        assert st == 0, fa.fa_last_error()
-        assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+        for causal in (1, 0):
+            q = torch.randn(2, 70, 4, 64, device="cuda").to(dtype)
+            o = torch.full_like(q, 7.0)
+            lse = torch.zeros(2, 4, 70, device="cuda")
+            # Nk = 0 still needs valid (non-NULL) pointers: pass q's storage.
+            st = (fa.fa_fwd if dtype == torch.bfloat16 else fa.fa_fwd_fp32)(
+                q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                2, 4, 2, 70, 0, 64, 0.125, causal, None, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert st == 0, fa.fa_last_error()
+            assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
 
 
 def test_noop_calls_leave_outputs_untouched():
@@ -217,10 +219,12 @@ def test_noop_calls_leave_outputs_untouched():
     assert bool((o == 3.0).all()) and bool((lse == 5.0).all())
 
 
-@pytest.mark.parametrize("wid", [3, 4])
+@pytest.mark.parametrize("wid", [2, 3, 4])
 def test_deterministic_bitwise(wid):
     """No atomics and a fixed reduction order: two identical calls at the
-    full workload size agree bit for bit (a mismatch would flag a race)."""
+    full workload size agree bit for bit (a mismatch would flag a race).
+    Workload 2 takes the key-halves schedule, whose two wave pairs hand
+    their partial state over through LDS."""
     import torch
     say(f"[case] determinism workload {wid}")
     w = W.WORKLOADS[wid]
