@@ -117,17 +117,10 @@ static_assert(Plan<128>::valid() && Plan<64>::valid(), "block plan");
 // are indexed from the first of them, kb_base.
 // BIAS: an additive bf16 bias B joins the scores of the visible pairs
 // before the softmax ("Understanding FlashAttention Pt 1", section 0.2:
-// S = Q K^T / sqrt(d) + B). The [256 x 64] bias tile of a block goes
-// through LDS like K and V (buffer-to-LDS loads, one block ahead, two
-// slots; rows of 64 keys, 16-byte units XOR-swizzled by row % 8), and each
-// lane reads the runs of 4 keys of its own score registers from there;
-// scores then carry t = scale * s + b in natural units and the base-2
-// factor becomes log2(e). The mask is applied after the add, so bytes past
-// the keys of a row never reach a visible score. A block that reaches past
-// the last key reads its bias straight from memory in runs clamped to the
-// row instead: the buffer range check drops a whole 16-byte unit that
-// straddles the end of the valid range, which would zero the last valid
-// keys of the tile's last row.
+// S = Q K^T / sqrt(d) + B). Each lane loads the bias values of its own
+// score registers (runs of 4 consecutive keys, 8 bytes) straight into
+// registers, one block ahead; scores then carry t = scale * s + b in
+// natural units and the base-2 factor becomes log2(e).
 // SPLIT (no mask but the key count, no window, no bias): for grids that
 // would leave compute units idle, a workgroup owns 128 query rows and its
 // two wave pairs take the first and the second half of the key blocks;
@@ -151,8 +144,6 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[NH * T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[NH * T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb1[NH * T::kBytes];
-  constexpr int kBiasTile = kBR * kBC * 2;  // bytes of one block's bias tile
-  __shared__ __attribute__((aligned(1024))) unsigned char bsd[BIAS ? 2 * kBiasTile : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,37 +265,40 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   const float ce = BIAS ? 1.4426950408889634f : c;
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // Bias tile of key block jb into LDS slot `slot`: rows q0 .. q0+255 of
-  // the workgroup, keys k0 .. k0+63. Each lane moves 8 units of 16 bytes (8
-  // keys); LDS unit u of row r holds global unit u ^ (r % 8). The buffer
-  // range ends at key Lk of the last valid row: rows past the queries read
-  // as zeros, and keys past Lk of other rows are masked after the add.
-  const u16* bg = BIAS ? static_cast<const u16*>(p.bias) + b * p.bias_sb + h * p.bias_sh : nullptr;
-  // This lane's bias rows, one per query tile (rows past the end read the
-  // last row; they are never stored), for the blocks past the last key.
+  // Bias rows of this lane, one per query tile (rows past the end read the
+  // last row; they are never stored), and the bias values of one block:
+  // bb[qt][kt][g] holds keys k0 + 32kt + 8g + 4*h2 + (0..3), i.e. score
+  // registers 4g .. 4g+3 of sc[qt][kt]. A run never crosses the end of a
+  // row: the row stride is a multiple of 4 and at least Nk, and in a block
+  // that reaches past the keys every run start is clamped to the last run.
   const u16* brow[2] = {nullptr, nullptr};
+  u32x2 bb[2][2][4];
   if constexpr (BIAS) {
+    const u16* bg = static_cast<const u16*>(p.bias) + b * p.bias_sb + h * p.bias_sh;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
       brow[qt] = bg + static_cast<long>(min(wq0 + 32 * qt + j, Lq - 1)) * p.bias_sr + 4 * h2;
   }
-  auto issue_bias = [&](int jb, int slot) {
+  auto load_bias = [&](int jb) {
     const int k0 = key_base + jb * kBC;
-    const long sr = p.bias_sr;
-    const int rows = min(Lq - q0, kBR);
-    const uint32_t nrec =
-        static_cast<uint32_t>((static_cast<long>(rows - 1) * sr + min(Lk - k0, kBC)) * 2);
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<u16*>(bg + static_cast<long>(q0) * sr + k0), 0, nrec, kBufferFlags);
+    if (k0 + kBC <= Lk) {
 #pragma unroll
-    for (int it = 0; it < kBiasTile / (16 * kThreads); ++it) {
-      const int u = it * kThreads + tid;
-      const int row = u >> 3;
-      const int gc = (u & 7) ^ (row & 7);
-      const uint32_t voff = static_cast<uint32_t>(row * sr * 2) + gc * 16;
-      const int lds_off = slot * kBiasTile + (it * kThreads + w * 64) * 16;  // wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(bsd + lds_off), 16, voff, 0,
-                                               0, 0);
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bb[qt][kt][g] = *reinterpret_cast<const u32x2*>(brow[qt] + k0 + 32 * kt + 8 * g);
+    } else {
+      const int kmax = ((Lk - 1) & ~3) - 4 * h2;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            bb[qt][kt][g] =
+                *reinterpret_cast<const u32x2*>(brow[qt] + min(k0 + 32 * kt + 8 * g, kmax));
     }
   };
 
@@ -326,7 +320,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   }
   asm volatile("s_nop 4" ::: "memory");     // AGPR writes before MFMA reads
   if constexpr (BIAS) {
-    if (nblk > 0) issue_bias(0, 0);
+    if (nblk_w > 0) load_bias(0);
   }
 
   f32x16 acc[2][ND];
@@ -413,9 +407,6 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       if (jb + 1 < nbh[h])
         issue_tile<D>(vg, kstride, hk(h) + (jb + 1) * kBC, Lk, v_free + h * T::kBytes, tid, w);
     }
-    if constexpr (BIAS) {  // slot PAR ^ 1 held block j-1's bias, consumed
-      if (jb + 1 < nblk) issue_bias(jb + 1, PAR ^ 1);
-    }
   };
   auto body = [&](auto par_tag, int jb, f32x16(&sc)[2][2], f32x16(&sn)[2][2]) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
@@ -440,49 +431,6 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       });
     };
 
-    if constexpr (BIAS) {  // t = cn * s + b, before the mask
-      // this lane's runs: keys k0 + 32kt + 8g + 4*h2 + (0..3) of its rows,
-      // bias[qt][kt][g], from LDS, or for a block past the last key from
-      // memory, each run start clamped to the last run of the row (a run
-      // never crosses the end of a row: the row stride is a multiple of 4
-      // and at least Nk)
-      u32x2 bias[2][2][4];
-      if (k0 + kBC <= Lk) {
-        const unsigned char* bt = bsd + PAR * kBiasTile;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const int lrow = 64 * w + 32 * qt + j;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              bias[qt][kt][g] = *reinterpret_cast<const u32x2*>(
-                  bt + lrow * (kBC * 2) + (((4 * kt + g) ^ (lrow & 7)) << 4) + 8 * h2);
-        }
-      } else {
-        const int kmax = ((Lk - 1) & ~3) - 4 * h2;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              bias[qt][kt][g] =
-                  *reinterpret_cast<const u32x2*>(brow[qt] + min(k0 + 32 * kt + 8 * g, kmax));
-      }
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t wd = bias[qt][kt][g][e >> 1];
-              const float bv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-              sc[qt][kt][4 * g + e] = __builtin_fmaf(sc[qt][kt][4 * g + e], cn, bv);
-            }
-    }
     // Only blocks that reach past the end of the keys or cross the causal
     // diagonal of this wave are masked: visible iff key <= lim, with
     // key - k0 - 4*h2 = 32kt + 8(r/4) + (r%4). c >= FLT_MIN keeps
@@ -521,6 +469,21 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
             }
         }
       }
+    }
+    if constexpr (BIAS) {  // t = cn * s + b; masked scores stay -inf
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wd = bb[qt][kt][g][e >> 1];
+              const float bv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+              sc[qt][kt][4 * g + e] = __builtin_fmaf(sc[qt][kt][4 * g + e], cn, bv);
+            }
+      if (jb + 1 < nblk_w) load_bias(jb + 1);
     }
     float mb[2];
     bool up = false;
