@@ -13,10 +13,11 @@
 //   dQ = scale dS K,   dK = scale dS^T Q
 // (D_i equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j).
 //
-// Three kernels, launched in order on one stream:
+// Two launches in order on one stream: bwd_dot_kernel, then
+// bwd_main_kernel, whose workgroups run one of two bodies:
 //   * bwd_dot_kernel: D = rowsum(dO * O) in float32, one value per (query
 //     row, q-head), laid out like the LSE;
-//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch or sequence,
+//   * dK/dV body: a workgroup owns 128 keys of one (batch or sequence,
 //     K/V head); wave w holds keys 32w .. 32w+31 of K and V in registers and
 //     accumulates dK^T and dV^T in registers while 64-row blocks of Q and dO
 //     (and their LSE and D) stream through LDS, for every query head of the
@@ -25,7 +26,7 @@
 //     registers = queries), then P and dS, packed to bf16 as the B operands
 //     of dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from the
 //     row-major LDS tiles through ds_read_b64_tr_b16;
-//   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch or
+//   * dQ body: a workgroup owns 128 query rows of one (batch or
 //     sequence, q-head); wave w holds rows 32w .. 32w+31 of Q and dO in
 //     registers (lane = query, one LSE and one D value per lane) and
 //     accumulates dQ^T while 64-key blocks of K and V stream through LDS:
@@ -207,9 +208,9 @@ __device__ __forceinline__ float bf16_bits_to_float(u16 x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
+// dK/dV of workgroup `bid` (see bwd_main_kernel for the launch).
 template <int D, bool CAUSAL, bool WIN, bool BIAS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdParams p, int n_kt) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int bid) {
   using T = Tile<D>;
   constexpr int NC = D / 16;  // 16-wide d chunks of the score contractions
   constexpr int ND = D / 32;  // 32-row d tiles of dK^T, dV^T
@@ -228,9 +229,9 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
   // the start of a sequence see the most queries under the causal mask and
   // go first.
   const int units = p.batch * p.hkv;
-  const int kt = static_cast<int>(blockIdx.x / units);
-  const int b = static_cast<int>(blockIdx.x % units) / p.hkv;
-  const int kvh = static_cast<int>(blockIdx.x % units) % p.hkv;
+  const int kt = bid / units;
+  const int b = (bid % units) / p.hkv;
+  const int kvh = (bid % units) % p.hkv;
   const int gq = p.hq / p.hkv;
   const SeqBounds sb = seq_bounds(p, b);
   const int k0 = kt * kBwdRows;
@@ -419,9 +420,9 @@ void bwd_dkdv_kernel(BwdParams p, int n_kt) {
 // dQ
 // ---------------------------------------------------------------------------
 
+// dQ of workgroup `bid` (see bwd_main_kernel for the launch).
 template <int D, bool CAUSAL, bool WIN, bool BIAS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dq_kernel(BwdParams p, int n_qt) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bid) {
   using T = Tile<D>;
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
@@ -437,9 +438,9 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
   // Workgroup -> (query tile, batch-or-sequence, q-head), longest causal
   // tiles first.
   const int bh = p.hq * p.batch;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x / bh);
-  const int b = static_cast<int>(blockIdx.x % bh) / p.hq;
-  const int h = static_cast<int>(blockIdx.x % bh) % p.hq;
+  const int qt = n_qt - 1 - bid / bh;
+  const int b = (bid % bh) / p.hq;
+  const int h = (bid % bh) % p.hq;
   const int kvh = h / (p.hq / p.hkv);
   const SeqBounds sb = seq_bounds(p, b);
   const int q0 = qt * kBwdRows;
@@ -597,12 +598,26 @@ void bwd_dq_kernel(BwdParams p, int n_qt) {
   }
 }
 
+// Both gradient kernels in one launch: they depend on the row dots D but
+// not on each other, so workgroups 0 .. n_dkdv-1 run the dK/dV body (the
+// longest key tiles first) and the rest the dQ body (the longest query
+// tiles first). Short dQ tiles then fill compute units as the long dK/dV
+// tiles finish, instead of each kernel draining its own tail. Either part
+// may be empty.
+template <int D, bool CAUSAL, bool WIN, bool BIAS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_main_kernel(BwdParams p, int n_qt, int n_kt, int n_dkdv) {
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < n_dkdv) bwd_dkdv_body<D, CAUSAL, WIN, BIAS>(p, n_kt, bid);
+  else bwd_dq_body<D, CAUSAL, WIN, BIAS>(p, n_qt, bid - n_dkdv);
+}
+
 }  // namespace
 
 // One object file per (head width, causal) pair, like the forward kernels.
-// An empty side launches nothing for it: with Nq == 0 the dK/dV kernel
-// still runs and writes zeros (no query sees any key), with Nk == 0 the dQ
-// kernel writes zeros.
+// An empty side launches no workgroups for it: with Nq == 0 only dK/dV
+// workgroups run and write zeros (no query sees any key), with Nk == 0
+// only dQ workgroups run and write zeros.
 template <int D, bool CAUSAL, bool WIN, bool BIAS>
 hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
   const long n_rows = static_cast<long>(p.batch) * p.nq * p.hq;
@@ -612,21 +627,16 @@ hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
                        dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_qt = (p.nq + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WIN, BIAS>),
-                       dim3(static_cast<unsigned>(n_qt) * p.hq * p.batch), dim3(kThreads), 0,
-                       stream, p, n_qt);
-    const hipError_t e2 = hipGetLastError();
-    if (e2 != hipSuccess) return e2;
   }
-  if (p.nk > 0) {
-    const int n_kt = (p.nk + kBwdRows - 1) / kBwdRows;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, WIN, BIAS>),
-                       dim3(static_cast<unsigned>(n_kt) * p.hkv * p.batch), dim3(kThreads), 0,
-                       stream, p, n_kt);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  const int n_qt = (p.nq + kBwdRows - 1) / kBwdRows;
+  const int n_kt = (p.nk + kBwdRows - 1) / kBwdRows;
+  const long n_dq = n_rows > 0 ? static_cast<long>(n_qt) * p.hq * p.batch : 0;
+  const long n_dkdv = p.nk > 0 ? static_cast<long>(n_kt) * p.hkv * p.batch : 0;
+  if (n_dq + n_dkdv == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, WIN, BIAS>),
+                     dim3(static_cast<unsigned>(n_dkdv + n_dq)), dim3(kThreads), 0, stream, p,
+                     n_qt, n_kt, static_cast<int>(n_dkdv));
+  return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
