@@ -214,10 +214,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
   using T = Tile<D>;
   constexpr int NC = D / 16;  // 16-wide d chunks of the score contractions
   constexpr int ND = D / 32;  // 32-row d tiles of dK^T, dV^T
-  __shared__ __attribute__((aligned(1024))) unsigned char q_st[2][T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_st[2][T::kBytes];
-  __shared__ __attribute__((aligned(16))) float lse_st[2][kTileRows];
-  __shared__ __attribute__((aligned(16))) float d_st[2][kTileRows];
+  // Two slots per staged tensor as separate arrays, chosen at compile time
+  // (the block loop is unrolled by two): with one array indexed at run time
+  // the compiler cannot tell the slot being loaded from the slot being read
+  // and waits for the next block's loads before every read of this one.
+  __shared__ __attribute__((aligned(1024))) unsigned char q_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_st1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_st1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) float lse_st0[kTileRows];
+  __shared__ __attribute__((aligned(16))) float lse_st1[kTileRows];
+  __shared__ __attribute__((aligned(16))) float d_st0[kTileRows];
+  __shared__ __attribute__((aligned(16))) float d_st1[kTileRows];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,13 +289,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
   const float c = p.scale_log2;
 
   auto head_of = [&](int it) { return kvh * gq + it / nqb; };
-  auto issue = [&](int it, int buf) {
+  auto issue = [&](int it, unsigned char* q_dst, unsigned char* do_dst, float* lse_dst,
+                   float* d_dst) {
     const int h = head_of(it);
     const int q0 = qb0 + (it % nqb) * kTileRows;
     const u16* qg = static_cast<const u16*>(p.q) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
     const u16* dg = static_cast<const u16*>(p.dout) + sb.q_tok0 * qstride + static_cast<long>(h) * D;
-    issue_tile<D>(qg, qstride, q0, sb.Lq, q_st[buf], tid, w);
-    issue_tile<D>(dg, qstride, q0, sb.Lq, do_st[buf], tid, w);
+    issue_tile<D>(qg, qstride, q0, sb.Lq, q_dst, tid, w);
+    issue_tile<D>(dg, qstride, q0, sb.Lq, do_dst, tid, w);
     if (w < 2) {
       // 64 floats of LSE (wave 0) or D (wave 1): one 4-byte load per lane
       const RowIndex ri = row_index(p, sb, b, h);
@@ -295,20 +304,25 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
       const int rows = min(sb.Lq - q0, kTileRows);
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(src), 0, static_cast<uint32_t>(rows) * 4u, kBufferFlags);
-      float* dst = w == 0 ? lse_st[buf] : d_st[buf];
+      float* dst = w == 0 ? lse_dst : d_dst;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
     }
   };
 
-  if (n_it > 0) issue(0, 0);
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
+  if (n_it > 0) issue(0, q_st0, do_st0, lse_st0, d_st0);
+  auto step = [&](auto par_tag, int it) {
+    constexpr int PAR = decltype(par_tag)::value;  // it & 1
     const int q0 = qb0 + (it % nqb) * kTileRows;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block `it` landed; every wave is done with block it-1
-    if (it + 1 < n_it) issue(it + 1, buf ^ 1);
-    const unsigned char* qs = q_st[buf];
-    const unsigned char* ds_ = do_st[buf];
+    if (it + 1 < n_it) {
+      if constexpr (PAR) issue(it + 1, q_st0, do_st0, lse_st0, d_st0);
+      else issue(it + 1, q_st1, do_st1, lse_st1, d_st1);
+    }
+    const unsigned char* qs = PAR ? q_st1 : q_st0;
+    const unsigned char* ds_ = PAR ? do_st1 : do_st0;
+    const float* ls = PAR ? lse_st1 : lse_st0;
+    const float* dsm = PAR ? d_st1 : d_st0;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int r0 = 32 * sub;  // tile row of this 32-row sub-block
@@ -350,8 +364,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int rr = r0 + 8 * g4 + 4 * h2;
-          const float4 l4 = *reinterpret_cast<const float4*>(&lse_st[buf][rr]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&d_st[buf][rr]);
+          const float4 l4 = *reinterpret_cast<const float4*>(ls + rr);
+          const float4 d4 = *reinterpret_cast<const float4*>(dsm + rr);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -385,6 +399,15 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
           asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
         }
       }
+    }
+  };
+  {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (int it = 0; it < n_it; it += 2) {
+      step(P0{}, it);
+      if (it + 1 >= n_it) break;
+      step(P1{}, it + 1);
     }
   }
 
@@ -426,8 +449,12 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
   using T = Tile<D>;
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st[2][T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st[2][T::kBytes];
+  // two slots per tensor, separate arrays chosen at compile time (see the
+  // dK/dV body)
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -500,19 +527,21 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
   }
   const int nkb = kend > key_base ? (kend - key_base + kTileRows - 1) / kTileRows : 0;
   if (nkb > 0) {
-    issue_tile<D>(kg, kstride, key_base, sb.Lk, k_st[0], tid, w);
-    issue_tile<D>(vg, kstride, key_base, sb.Lk, v_st[0], tid, w);
+    issue_tile<D>(kg, kstride, key_base, sb.Lk, k_st0, tid, w);
+    issue_tile<D>(vg, kstride, key_base, sb.Lk, v_st0, tid, w);
   }
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  auto step = [&](auto par_tag, int kb) {
+    constexpr int PAR = decltype(par_tag)::value;  // kb & 1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 < nkb) {
-      issue_tile<D>(kg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, k_st[buf ^ 1], tid, w);
-      issue_tile<D>(vg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, v_st[buf ^ 1], tid, w);
+      unsigned char* k_nxt = PAR ? k_st0 : k_st1;
+      unsigned char* v_nxt = PAR ? v_st0 : v_st1;
+      issue_tile<D>(kg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, k_nxt, tid, w);
+      issue_tile<D>(vg, kstride, key_base + (kb + 1) * kTileRows, sb.Lk, v_nxt, tid, w);
     }
-    const unsigned char* ks = k_st[buf];
-    const unsigned char* vs = v_st[buf];
+    const unsigned char* ks = PAR ? k_st1 : k_st0;
+    const unsigned char* vs = PAR ? v_st1 : v_st0;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int r0 = 32 * sub;
@@ -576,6 +605,15 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
           asm volatile("" : "+a"(dq[t]));
         }
       }
+    }
+  };
+  {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (int kb = 0; kb < nkb; kb += 2) {
+      step(P0{}, kb);
+      if (kb + 1 >= nkb) break;
+      step(P1{}, kb + 1);
     }
   }
 

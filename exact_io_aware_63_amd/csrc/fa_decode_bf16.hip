@@ -78,8 +78,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   using T = Tile<D>;
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;  // d-tiles of O^T; waves >= ND idle in the P V product
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st[2][T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st[2][T::kBytes];
+  // Two slots per tensor as separate arrays, chosen at compile time (the
+  // loop is unrolled by two): with one array indexed at run time the
+  // compiler cannot tell the slot being loaded from the slot being read,
+  // and waits for the new tile's loads before every read of the current one.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,17 +132,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
   const int nkb = (kend - kbeg + kTileRows - 1) / kTileRows;
   if (nkb > 0) {
-    issue_tile<D>(kg, kstride, kbeg, kend, k_st[0], tid, w);
-    issue_tile<D>(vg, kstride, kbeg, kend, v_st[0], tid, w);
+    issue_tile<D>(kg, kstride, kbeg, kend, k_st0, tid, w);
+    issue_tile<D>(vg, kstride, kbeg, kend, v_st0, tid, w);
   }
-  for (int it = 0; it < nkb; ++it) {
-    const int buf = it & 1;
+  auto step = [&](auto par_tag, int it) {
+    constexpr int PAR = decltype(par_tag)::value;  // it & 1
+    const unsigned char* k_cur = PAR ? k_st1 : k_st0;
+    const unsigned char* v_cur = PAR ? v_st1 : v_st0;
+    unsigned char* k_nxt = PAR ? k_st0 : k_st1;
+    unsigned char* v_nxt = PAR ? v_st0 : v_st1;
     const int k0 = kbeg + it * kTileRows;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (it + 1 < nkb) {
-      issue_tile<D>(kg, kstride, k0 + kTileRows, kend, k_st[buf ^ 1], tid, w);
-      issue_tile<D>(vg, kstride, k0 + kTileRows, kend, v_st[buf ^ 1], tid, w);
+      issue_tile<D>(kg, kstride, k0 + kTileRows, kend, k_nxt, tid, w);
+      issue_tile<D>(vg, kstride, k0 + kTileRows, kend, v_nxt, tid, w);
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       f32x16 st = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand_dec<D>(k_st[buf], 32 * sub, cc, lane),
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand_dec<D>(k_cur, 32 * sub, cc, lane),
                                                      qf[cc], st, 0, 0, 0);
       // x = c * s on visible keys, -inf elsewhere
       float mx = -INFINITY;
@@ -176,11 +186,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
           bf16x8 pb;
 #pragma unroll
           for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(pr[8 * g + i]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand_dec<D>(v_st[buf], 32 * sub, w, g, lane),
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand_dec<D>(v_cur, 32 * sub, w, g, lane),
                                                         pb, acc, 0, 0, 0);
         }
       }
     }
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  for (int it = 0; it < nkb; it += 2) {
+    step(P0{}, it);
+    if (it + 1 >= nkb) break;
+    step(P1{}, it + 1);
   }
 
   // Partial results of this split: o_s = a / l (float32) and LSE_s (natural
