@@ -5,7 +5,8 @@ HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
 The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_fwd_window``, ``fa_fwd_bias``,
-``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_fwd_fp8``, ``fa_status_string``,
+``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_fwd_fp8``,
+``fa_check_cu_seqlens``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
 wrapper that checks torch tensors, allocates O and LSE with torch and calls
@@ -22,7 +23,9 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# FA_LIBRARY names another build of the same library (the host-sanitized
+# one, say); by default the in-tree libfa.so is loaded.
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 FA_OK = 0
 FA_ERR_NULL = -1
@@ -80,13 +83,16 @@ _lib.fa_status_string.argtypes = [ctypes.c_int]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
+_lib.fa_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+_lib.fa_check_cu_seqlens.restype = ctypes.c_int
 _lib.fa_version.argtypes = []
 _lib.fa_version.restype = ctypes.c_int
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
             "fa_bwd_bias",
             "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_fp8",
-            "fa_fwd_fp8_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version")
+            "fa_fwd_fp8_workspace_bytes", "fa_check_cu_seqlens", "fa_status_string",
+            "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -188,12 +194,21 @@ def attention_fwd_fp8(q, k, v, *, q_descale=1.0, k_descale=1.0, v_descale=1.0,
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise TypeError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn)")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q and k disagree on B or d")
+    if d != 128:
+        raise ValueError(f"the fp8 forward takes d=128, got d={d}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -210,6 +225,12 @@ def attention_fwd_fp8(q, k, v, *, q_descale=1.0, k_descale=1.0, v_descale=1.0,
     return out, lse
 
 
+def fa_check_cu_seqlens(cu_seqlens_host, B, max_seqlen) -> int:
+    """C ``fa_check_cu_seqlens``: ``cu_seqlens_host`` is an integer HOST
+    address of int32 [B + 1] (or 0 / None)."""
+    return _lib.fa_check_cu_seqlens(cu_seqlens_host, B, max_seqlen)
+
+
 def fa_status_string(status: int) -> str:
     return _lib.fa_status_string(status).decode()
 
@@ -220,6 +241,25 @@ def fa_last_error() -> str:
 
 def fa_version() -> int:
     return _lib.fa_version()
+
+
+def _check_outputs(q, out, lse, lse_shape):
+    """Caller-supplied output buffers must be exactly what the kernels write:
+    ``out`` like q (shape, dtype, contiguous), ``lse`` float32 of
+    ``lse_shape``, contiguous. Devices are compared with q's afterwards."""
+    import torch
+    if out is not None:
+        if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+            raise ValueError(f"out must match q: shape {tuple(q.shape)}, dtype {q.dtype}; got "
+                             f"{tuple(out.shape)}, {out.dtype}")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    if lse is not None:
+        if tuple(lse.shape) != tuple(lse_shape) or lse.dtype != torch.float32:
+            raise ValueError(f"lse must be float32 of shape {tuple(lse_shape)}; got "
+                             f"{tuple(lse.shape)}, {lse.dtype}")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous")
 
 
 def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
@@ -246,11 +286,6 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
         fn = _lib.fa_fwd_fp32
     else:
         raise TypeError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if cu_seqlens is None:
         if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
             raise ValueError("fixed length wants q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]")
@@ -263,7 +298,7 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
     else:
         if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
             raise ValueError("packed wants q [T,Hq,d], k/v [T,Hkv,d]")
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
             raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
         if max_seqlen is None:
             raise ValueError("packed input needs max_seqlen (host int)")
@@ -275,6 +310,18 @@ def attention_fwd(q, k, v, *, causal: bool = False, scale=None, cu_seqlens=None,
         Nq = Nk = int(max_seqlen)
         lse_shape = (Hq, T)
         cu_ptr = cu_seqlens.data_ptr()
+    _check_outputs(q, out, lse, lse_shape)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens), ("out", out),
+                    ("lse", lse)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:

@@ -77,5 +77,38 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(OBJ_DIR, "libfa_sanitized.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C
+    ABI layer: ``fa_api.cpp`` is compiled with g++ and the sanitizers (host
+    code only; the kernel objects of ``build()`` are linked as they are) into
+    ``_build/libfa_sanitized.so``. Load it with the ASan runtime preloaded and
+    ``FA_LIBRARY`` pointing at it to run the ABI tests under the sanitizers."""
+    objs = [os.path.join(OBJ_DIR, name + ".o") for _, name, _ in SOURCES if name != "fa_api"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"kernel objects missing (run build() first): {missing[:2]}")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    api_obj = os.path.join(OBJ_DIR, "fa_api_sanitized.o")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer"]
+    steps = [
+        ["g++", "-std=c++17", "-O1", "-g", "-fPIC", *san, "-D__HIP_PLATFORM_AMD__",
+         f"-I{rocm}/include", "-c", "-o", api_obj, os.path.join(CSRC, "fa_api.cpp")],
+        ["g++", "-shared", "-fPIC", *san, "-o", SANITIZED_LIB, api_obj, *objs,
+         f"-L{rocm}/lib", "-lamdhip64", f"-Wl,-rpath,{rocm}/lib"],
+    ]
+    for cmd in steps:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"sanitized build failed: {cmd[0]} exit {res.returncode}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

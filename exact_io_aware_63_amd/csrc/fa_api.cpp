@@ -9,8 +9,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/fa.h"
 #include "fa_launch.h"
@@ -128,6 +130,48 @@ int validate_bias(const BiasArg& b, int Nk) {
   return FA_OK;
 }
 
+// Packed offsets in host memory: 0 first, non-decreasing, no sequence
+// longer than max_seqlen.
+int check_cu_host(const int32_t* cu, int B, int max_seqlen) {
+  if (B < 0) return fail(FA_ERR_SHAPE, "B=%d must be >= 0", B);
+  if (B == 0) return FA_OK;
+  if (cu == nullptr) return fail(FA_ERR_NULL, "cu_seqlens is NULL");
+  if (cu[0] != 0) return fail(FA_ERR_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int s = 0; s < B; ++s) {
+    const long len = static_cast<long>(cu[s + 1]) - cu[s];
+    if (len < 0)
+      return fail(FA_ERR_ARG, "cu_seqlens decreases at %d: %d then %d", s, cu[s], cu[s + 1]);
+    if (len > max_seqlen)
+      return fail(FA_ERR_ARG, "sequence %d has %ld tokens, more than max_seqlen=%d", s, len,
+                  max_seqlen);
+  }
+  return FA_OK;
+}
+
+// FA_CHECK_INPUTS set (and not "0"): copy the device cu_seqlens to the host
+// on the call's stream, wait for it, and check it before any launch.
+int check_cu_device_if_asked(const int32_t* cu, int B, int max_seqlen, hipStream_t stream) {
+  const char* env = std::getenv("FA_CHECK_INPUTS");
+  if (cu == nullptr || env == nullptr || env[0] == '\0' || std::strcmp(env, "0") == 0)
+    return FA_OK;
+  std::vector<int32_t> host(static_cast<size_t>(B) + 1);
+  hipError_t e = hipMemcpyAsync(host.data(), cu, host.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "copying cu_seqlens to the host failed: %s", hipGetErrorString(e));
+  return check_cu_host(host.data(), B, max_seqlen);
+}
+
+// A window bound of max(Nq, Nk) or more restricts nothing (local indices
+// differ by less than that), so larger bounds are clamped there: the
+// kernels then form i + bound without int overflow. -1 (any negative)
+// stays "unbounded".
+int clamp_window(int bound, int Nq, int Nk) {
+  if (bound < 0) return -1;
+  return std::min(bound, std::max(Nq, Nk));
+}
+
 int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
         int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* cu_seqlens,
         void* stream, int win_left = -1, int win_right = -1, const BiasArg* bias = nullptr) {
@@ -137,8 +181,12 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   int st = validate(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, cu_seqlens, tile_rows, &noop);
   if (st != FA_OK || noop) return st;
   if (bias != nullptr && (st = validate_bias(*bias, Nk)) != FA_OK) return st;
+  if ((win_left >= 0 || win_right >= 0) && std::max(Nq, Nk) > (1 << 30))
+    return fail(FA_ERR_SHAPE, "a sliding window needs Nq, Nk <= 2^30");
   int cus = 0;
   st = check_device(&cus);
+  if (st != FA_OK) return st;
+  st = check_cu_device_if_asked(cu_seqlens, B, Nq, static_cast<hipStream_t>(stream));
   if (st != FA_OK) return st;
   fa::FwdParams p;
   p.num_cus = cus;
@@ -156,8 +204,8 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   p.d = d;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.causal = causal ? 1 : 0;
-  p.win_left = win_left < 0 ? -1 : win_left;
-  p.win_right = win_right < 0 ? -1 : win_right;
+  p.win_left = clamp_window(win_left, Nq, Nk);
+  p.win_right = clamp_window(win_right, Nq, Nk);
   p.scale = scale;
   p.bias = bias ? bias->ptr : nullptr;
   p.bias_sb = bias ? bias->sb : 0;
@@ -227,7 +275,11 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
                         cu_seqlens, &noop);
   if (st != FA_OK || noop) return st;
   if (bias != nullptr && (st = validate_bias(*bias, Nk)) != FA_OK) return st;
+  if ((win_left >= 0 || win_right >= 0) && std::max(Nq, Nk) > (1 << 30))
+    return fail(FA_ERR_SHAPE, "a sliding window needs Nq, Nk <= 2^30");
   st = check_device();
+  if (st != FA_OK) return st;
+  st = check_cu_device_if_asked(cu_seqlens, B, Nq, static_cast<hipStream_t>(stream));
   if (st != FA_OK) return st;
   fa::BwdParams p;
   p.q = Q;
@@ -250,8 +302,8 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   p.scale = scale;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.causal = causal ? 1 : 0;
-  p.win_left = win_left < 0 ? -1 : win_left;
-  p.win_right = win_right < 0 ? -1 : win_right;
+  p.win_left = clamp_window(win_left, Nq, Nk);
+  p.win_right = clamp_window(win_right, Nq, Nk);
   p.bias = bias ? bias->ptr : nullptr;
   p.bias_sb = bias ? bias->sb : 0;
   p.bias_sh = bias ? bias->sh : 0;
@@ -493,6 +545,11 @@ const char* fa_status_string(int status) {
 }
 
 const char* fa_last_error(void) { return g_last_error; }
+
+int fa_check_cu_seqlens(const int32_t* cu_seqlens_host, int B, int max_seqlen) {
+  g_last_error[0] = '\0';
+  return check_cu_host(cu_seqlens_host, B, max_seqlen);
+}
 
 int fa_version(void) { return kVersion; }
 

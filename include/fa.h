@@ -57,8 +57,12 @@
  * any HIP call. fa_last_error() gives a thread-local message for the last
  * failing call on this thread. Device-side faults are asynchronous and
  * surface at the caller's next synchronisation. The contents of cu_seqlens
- * live on the device and are not checked: offsets that are decreasing or
- * exceed the buffers are undefined behaviour.
+ * live on the device and are not checked by default: offsets that are
+ * decreasing or exceed the buffers are undefined behaviour. With the
+ * environment variable FA_CHECK_INPUTS set to a value other than "0", every
+ * call that takes cu_seqlens first copies it to the host (synchronising
+ * `stream`) and checks it with fa_check_cu_seqlens; a bad array fails the
+ * call with FA_ERR_ARG before any kernel is launched.
  */
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
@@ -269,6 +273,16 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                float q_descale, float k_descale, float v_descale, int causal,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side check of a packed-sequence offset array (the one fa_fwd and
+ * fa_bwd take as cu_seqlens), here in HOST memory: cu_seqlens_host[0] == 0,
+ * non-decreasing, and no sequence longer than max_seqlen. Returns FA_OK,
+ * FA_ERR_NULL (NULL array with B > 0), FA_ERR_SHAPE (B < 0) or FA_ERR_ARG
+ * (the first violation, named in fa_last_error()). Reads B + 1 values; no
+ * HIP call.
+ */
+int fa_check_cu_seqlens(const int32_t* cu_seqlens_host, int B, int max_seqlen);
 
 /* Static text for a status code. */
 const char* fa_status_string(int status);

@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
          "fa_bwd_bias", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes",
-         "fa_fwd_splitkv_workspace_bytes",
+         "fa_fwd_splitkv_workspace_bytes", "fa_check_cu_seqlens",
          "fa_status_string", "fa_last_error", "fa_version"])
 
 
@@ -359,3 +359,101 @@ def test_fp8_noop_and_no_gpu(fa):
         assert _call_fp8(fa) == fa.FA_ERR_HIP
         assert _call_fp8(fa, Nk=0, k=0, v=0, ws=0, wsb=0) == fa.FA_ERR_HIP
 
+
+
+def _call_window(fa, left, right, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], left, right,
+                            a["cu"], a["stream"])
+
+
+@pytest.mark.parametrize("left,right", [(2**31 - 1, 2**31 - 1), (2**31 - 1, -1), (0, 2**31 - 1),
+                                        (-5, -7)])
+def test_window_any_int_bound_passes_host_checks(fa, left, right):
+    """Bounds up to INT_MAX are legal (the host clamps them to max(Nq, Nk));
+    without a GPU the call gets as far as the device check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_window(fa, left, right) == fa.FA_ERR_HIP
+    assert _call_window(fa, left, right, causal=1, Nq=8, Nk=1000) == fa.FA_ERR_HIP
+
+
+def test_window_rejects_sequences_beyond_2_pow_30(fa):
+    """A window with Nq or Nk above 2^30 could overflow i + bound in int."""
+    big = (1 << 30) + 1
+    assert _call_window(fa, 4, 4, Hq=1, Hkv=1, Nq=big, Nk=8) == fa.FA_ERR_SHAPE
+    assert "2^30" in fa.fa_last_error()
+    assert _call_window(fa, -1, 4, Hq=1, Hkv=1, Nq=8, Nk=big) == fa.FA_ERR_SHAPE
+
+
+def test_attention_fwd_checks_output_buffers(fa):
+    """Wrong caller-supplied O or LSE buffers are refused before any call."""
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 4, dtype=torch.float32)
+    bad_out = [torch.zeros(1, 4, 2, 32, dtype=torch.bfloat16),      # shape
+               torch.zeros(1, 4, 2, 64, dtype=torch.float32),       # dtype
+               torch.zeros(1, 4, 64, 2, dtype=torch.bfloat16).transpose(2, 3)]  # layout
+    for out in bad_out:
+        with pytest.raises(ValueError, match="out"):
+            fa.attention_fwd(q, q, q, out=out, lse=lse)
+    bad_lse = [torch.zeros(1, 4, 2, dtype=torch.float32),           # [B, Nq, Hq]
+               torch.zeros(1, 2, 4, dtype=torch.bfloat16),          # dtype
+               torch.zeros(1, 4, 2, dtype=torch.float32).transpose(1, 2)]  # layout
+    for l in bad_lse:
+        with pytest.raises(ValueError, match="lse"):
+            fa.attention_fwd(q, q, q, out=torch.zeros_like(q), lse=l)
+    # packed: LSE is [Hq, T]
+    qp = torch.zeros(6, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 2, 6], dtype=torch.int32)
+    with pytest.raises(ValueError, match="lse"):
+        fa.attention_fwd(qp, qp, qp, cu_seqlens=cu, max_seqlen=4,
+                         lse=torch.zeros(6, 2, dtype=torch.float32))
+    # right buffers on the host: refused only for not being device tensors
+    with pytest.raises(ValueError, match="device"):
+        fa.attention_fwd(q, q, q, out=torch.zeros_like(q), lse=lse)
+
+
+def test_attention_fwd_fp8_checks_shapes(fa):
+    import torch
+    q = torch.zeros(2, 4, 2, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="B or d"):
+        fa.attention_fwd_fp8(q, q[:1], q[:1])                       # batch differs
+    k = torch.zeros(2, 4, 2, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="B or d"):
+        fa.attention_fwd_fp8(q, k, k)                               # d differs
+    q64 = torch.zeros(2, 4, 2, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="d=128"):
+        fa.attention_fwd_fp8(q64, q64, q64)
+    with pytest.raises(ValueError, match="device"):
+        fa.attention_fwd_fp8(q, q, q)
+    with pytest.raises(TypeError):
+        fa.attention_fwd_fp8(q.float(), q, q)
+
+
+CU_CASES = [
+    ("valid", [0, 3, 3, 10], 7, 0),
+    ("valid_empty_batch", [0], 7, 0),
+    ("first_not_zero", [1, 3, 10], 7, -4),
+    ("decreasing", [0, 5, 4, 10], 7, -4),
+    ("longer_than_max", [0, 3, 11], 7, -4),
+    ("exactly_max", [0, 7, 14], 7, 0),
+]
+
+
+@pytest.mark.parametrize("name,cu,mx,status", CU_CASES, ids=[c[0] for c in CU_CASES])
+def test_check_cu_seqlens(fa, name, cu, mx, status):
+    import numpy as np
+    a = np.asarray(cu, dtype=np.int32)
+    st = fa.fa_check_cu_seqlens(a.ctypes.data, len(cu) - 1, mx)
+    assert st == status, (st, fa.fa_last_error())
+    assert bool(fa.fa_last_error()) == (status != 0)
+
+
+def test_check_cu_seqlens_null_and_negative(fa):
+    assert fa.fa_check_cu_seqlens(None, 2, 8) == fa.FA_ERR_NULL
+    assert fa.fa_check_cu_seqlens(None, 0, 8) == fa.FA_OK
+    assert fa.fa_check_cu_seqlens(None, -1, 8) == fa.FA_ERR_SHAPE

@@ -305,3 +305,26 @@ def test_falling_scores_underflow_later_tiles():
     o, lse = run_gpu(inp, True, scale)
     o_ref, lse_ref = oracle.attention_ref(inp.q, inp.k, inp.v, scale, True)
     assert_parity(o, lse, o_ref, lse_ref, "bf16", "falling scores")
+
+
+def test_check_inputs_env_rejects_bad_offsets(monkeypatch):
+    """With FA_CHECK_INPUTS set, packed calls copy cu_seqlens to the host and
+    refuse a bad array before any launch. The bad arrays used here stay
+    inside the buffers (a sequence longer than max_seqlen, a first offset
+    that is not 0), so a launch would not read out of bounds either."""
+    import torch
+    fa = _fa()
+    say("[case] FA_CHECK_INPUTS on packed offsets")
+    T, hq, hkv, d = 6, 2, 1, 64
+    q = torch.zeros(T, hq, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(T, hkv, d, dtype=torch.bfloat16, device="cuda")
+    good = torch.tensor([0, 2, 6], dtype=torch.int32, device="cuda")
+    long_seq = torch.tensor([0, 6], dtype=torch.int32, device="cuda")
+    not_zero = torch.tensor([2, 6], dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("FA_CHECK_INPUTS", "1")
+    fa.attention_fwd(q, k, k, causal=True, cu_seqlens=good, max_seqlen=4)
+    for cu, mx, what in ((long_seq, 4, "max_seqlen"), (not_zero, 4, "must be 0")):
+        with pytest.raises(fa.FaError) as ei:
+            fa.attention_fwd(q, k, k, causal=True, cu_seqlens=cu, max_seqlen=mx)
+        assert ei.value.status == fa.FA_ERR_ARG and what in ei.value.detail
+    torch.cuda.synchronize()

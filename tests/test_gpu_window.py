@@ -80,8 +80,11 @@ def test_wide_window_is_fa_fwd():
         q, k, v, _ = to_device(inp)
         o1, l1 = fa.attention_fwd(q, k, v, causal=causal)
         o2, l2 = fa.attention_fwd(q, k, v, causal=causal, window=(5000, 5000))
+        # the widest bounds an int holds: the host clamps them to max(Nq, Nk)
+        o3, l3 = fa.attention_fwd(q, k, v, causal=causal, window=(2**31 - 1, 2**31 - 1))
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
 def test_window_workload4_sampled():
