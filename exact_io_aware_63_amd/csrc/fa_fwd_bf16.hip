@@ -332,7 +332,11 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       asm volatile("" : "+a"(acc[qt][t]));
     }
   float m_run[2] = {-INFINITY, -INFINITY};  // running reference of x = c * s
-  float l_run[2] = {0.f, 0.f};              // this lane's part of the denominator
+  float l_run[2] = {0.f, 0.f};              // this lane's part of l (unrounded weights)
+  // the same sum with each block's largest weight taken as the bf16 value
+  // that P V multiplies: O = a / lt cancels the rounding of a row's dominant
+  // weight (LSE keeps l)
+  float lt_run[2] = {0.f, 0.f};
 
   // Per-lane constants of the LDS reads.
   const int k_row_off = j * T::kRowBytes;            // + kt * 32 rows
@@ -485,7 +489,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
             }
       if (jb + 1 < nblk_w) load_bias(jb + 1);
     }
-    float mb[2];
+    float mb[2], smax[2];
     bool up = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -494,7 +498,8 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[qt][0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qt][1][r]);
-      mb[qt] = xhalf_max(mx) * ce;
+      smax[qt] = xhalf_max(mx);
+      mb[qt] = smax[qt] * ce;
       // A row's first visible block sets its reference (its accumulator and
       // denominator are still zero); later raises need the rescale.
       if (m_run[qt] == -INFINITY) m_run[qt] = mb[qt];
@@ -510,6 +515,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
         m_run[qt] = m_new;
         l_run[qt] *= alpha;
+        lt_run[qt] *= alpha;
 #pragma unroll
         for (int t = 0; t < ND; ++t) acc[qt][t] = scale_via_scratch(acc[qt][t], alpha);
       }
@@ -521,6 +527,13 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     float m_ref[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) m_ref[qt] = (m_run[qt] == -INFINITY) ? 0.f : m_run[qt];
+    // bf16 rounding residual of each row's largest weight of this block (the
+    // same arithmetic as that weight's own exponential below)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(smax[qt], ce, -m_ref[qt]));
+      lt_run[qt] += static_cast<float>(static_cast<__bf16>(pm)) - pm;
+    }
 
     // P^T as the B operand of O^T += V^T P^T: 16-key chunk g takes score
     // registers 8(g%2) .. 8(g%2)+7 of key tile g/2, i.e. keys
@@ -557,8 +570,10 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)  // from the unrounded float32 P
+    for (int qt = 0; qt < 2; ++qt) {
       l_run[qt] += (rs[qt][0] + rs[qt][1]) + (rs[qt][2] + rs[qt][3]);
+      lt_run[qt] += (rs[qt][0] + rs[qt][1]) + (rs[qt][2] + rs[qt][3]);
+    }
   };
 
   // Key loop, unrolled by two so every LDS address has a fixed buffer. A
@@ -596,6 +611,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         }
         ym[qt * 64 + lane] = m_run[qt];
         ym[(2 + qt) * 64 + lane] = l_run[qt];
+        ym[(4 + qt) * 64 + lane] = lt_run[qt];
       }
     }
     __syncthreads();
@@ -613,6 +629,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
       const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
       l_run[qt] = l_run[qt] * a0 + xm[(2 + qt) * 64 + lane] * a1;
+      lt_run[qt] = lt_run[qt] * a0 + xm[(4 + qt) * 64 + lane] * a1;
       m_run[qt] = mm;
 #pragma unroll
       for (int t = 0; t < ND; ++t)
@@ -622,8 +639,10 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     }
     const int qrow = wq0 + 32 * qt + j;
     const float l_tot = xhalf_sum(l_run[qt]);
+    const float lt_tot = xhalf_sum(lt_run[qt]);
     if (qrow < Lq) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      // o = a / lt, LSE from l
+      const float inv = l_tot > 0.f ? 1.f / lt_tot : 0.f;
       u16* og = static_cast<u16*>(p.o) + (q_tok0 + qrow) * qstride + static_cast<long>(h) * D;
 #pragma unroll
       for (int t = 0; t < ND; ++t)

@@ -92,3 +92,24 @@ def gather_picks(o, lse, picks, inp):
     cu = inp.cu_seqlens.astype(np.int64)
     tok = cu[picks[:, 0]] + picks[:, 2]
     return o[tok, picks[:, 1]], lse[picks[:, 1], tok]
+
+
+def oracle_sequence(q, k, v, scale, causal, workers=8):
+    """The fp64 oracle on every head of one sequence, heads run in a thread
+    pool (numpy's matrix products and exponentials release the GIL).
+    q [L, Hq, d], k and v [L, Hkv, d]; returns (O [L, Hq, d], LSE [Hq, L])."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    lq, hq, d = q.shape
+    hkv = k.shape[1]
+    out = np.zeros((lq, hq, d), dtype=np.float64)
+    lse = np.full((hq, lq), -np.inf)
+
+    def one(h):
+        g = oracle.kv_head_of(h, hq, hkv)
+        out[:, h], lse[h] = oracle.attention_head(q[:, h], k[:, g], v[:, g], scale, causal)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(hq)))
+    return out, lse

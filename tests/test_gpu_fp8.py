@@ -194,8 +194,9 @@ def test_fp8_deterministic_and_negative_scale():
 
 def test_fp8_full_size_sampled():
     """Causal GQA 32/8 heads, N = 8192, d = 128 (the bf16 workload's shape)
-    with amax-scaled N(0, 1) inputs; rows sampled at tile edges and at
-    random, each formed whole by the oracle, against the bound."""
+    with amax-scaled N(0, 1) inputs: 32 rows of every head (tile edges and
+    random rows, 1024 in all), each formed whole by the oracle, against the
+    bound."""
     import torch
 
     import exact_io_aware_63_amd as fa
@@ -206,21 +207,100 @@ def test_fp8_full_size_sampled():
                                   q_descale=x.q_descale, k_descale=x.k_descale,
                                   v_descale=x.v_descale, causal=True, scale=w.scale)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(4008)
-    rows = sorted({0, 1, 63, 64, 255, 256, 4095, 4096, w.n - 2, w.n - 1} |
-                  set(rng.integers(0, w.n, 14).tolist()))
-    picks = np.array([(0, int(rng.integers(w.hq)), i) for i in rows])
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
     q, k, v = _deq(x)
-    ro, rl = oracle.attention_picked(q, k, v, w.scale, True, picks)
-    bo = np.zeros_like(ro)
-    bl = np.zeros_like(rl)
-    for n, (s, h, i) in enumerate(picks):
-        g = oracle.kv_head_of(int(h), w.hq, w.hkv)
-        pabs, vsum, psv, ps = _row_terms(q[s, :, h], k[s, :, g], v[s, :, g], w.scale, True,
-                                         np.array([i]), ro[n:n + 1])
-        bo[n] = (2.0 ** -4 * pabs + 2.0 ** -17 * vsum + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
-                 2.0 ** -8 * np.abs(ro[n:n + 1]) + 1e-6)[0]
-        bl[n] = EPS * ps[0] + 1e-5 * (1 + abs(rl[n]))
-    go = o[0, picks[:, 2], picks[:, 1]].float().cpu().double().numpy()
-    gl = lse[0, picks[:, 1], picks[:, 2]].cpu().double().numpy()
-    _check("full size sampled", go, gl, ro, rl, bo, bl)
+    rng = np.random.default_rng(4008)
+    edges = {0, 1, 63, 64, 255, 256, 4095, 4096, w.n - 2, w.n - 1}
+    n_rows = 0
+    for h in range(w.hq):
+        rows = np.array(sorted(edges | set(rng.choice(w.n, 32 - len(edges) + 4,
+                                                      replace=False).tolist()))[:32])
+        g = oracle.kv_head_of(h, w.hq, w.hkv)
+        ro, rl = oracle.attention_head(q[0, :, h], k[0, :, g], v[0, :, g], w.scale, True,
+                                       rows=rows)
+        pabs, vsum, psv, ps = _row_terms(q[0, :, h], k[0, :, g], v[0, :, g], w.scale, True, rows,
+                                         ro)
+        bo = (2.0 ** -4 * pabs + 2.0 ** -17 * vsum + EPS * (1 + 2.0 ** -4) * pabs + EPS * psv +
+              2.0 ** -8 * np.abs(ro) + 1e-6)
+        bl = EPS * ps + 1e-5 * (1 + np.abs(rl))
+        _check(f"full size head {h}", o[0, rows, h], lse[0, h, rows], ro, rl, bo, bl)
+        n_rows += len(rows)
+    assert n_rows >= 1000
+
+
+def _codes(x):
+    """e4m3 codes of values that e4m3 holds exactly (checked)."""
+    b = W.to_e4m3_bits(np.asarray(x, np.float32))
+    assert np.array_equal(oracle.e4m3_value(b), np.asarray(x, np.float64)), "not exact in e4m3"
+    return b
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_far_rescale_every_block(causal):
+    """Scores that climb by about 82 (base 2) from one 64-key block to the
+    next: every block maximum lies more than 64 above the row's reference,
+    so each block moves the reference and rescales the accumulators (the
+    rare path kept for float32 range). Inputs have descale 1: N(0, 1) codes,
+    with q's last column 40 and key j's last column 16 floor(j / 64)."""
+    say(f"[case] fp8 far rescale every block, causal={causal}")
+    n, hq, hkv, d = 700, 4, 2, 128
+    rng = np.random.default_rng(77)
+    qv = oracle.e4m3_value(W.to_e4m3_bits(rng.standard_normal((1, n, hq, d), np.float32)))
+    kv = oracle.e4m3_value(W.to_e4m3_bits(rng.standard_normal((1, n, hkv, d), np.float32)))
+    vv = oracle.e4m3_value(W.to_e4m3_bits(rng.standard_normal((1, n, hkv, d), np.float32)))
+    qv[..., -1] = 40.0
+    kv[0, :, :, -1] = (16.0 * np.floor(np.arange(n) / 64.0))[:, None]
+    x = W.Fp8Inputs(_codes(qv), _codes(kv), _codes(vv), 1.0, 1.0, 1.0)
+    scale = 1.0 / math.sqrt(d)
+    # precondition, from the definition: consecutive full blocks' maxima
+    # (base 2) differ by more than 64 for every row of every head
+    for h in range(hq):
+        g = oracle.kv_head_of(h, hq, hkv)
+        s2 = oracle.scores(qv[0, :, h], kv[0, :, g], scale) * 1.4426950408889634
+        full = s2[:, :(n // 64) * 64].reshape(n, n // 64, 64).max(axis=2)
+        assert float(np.diff(full, axis=1).min()) > 64.0
+    o, lse = _run(x, causal, scale)
+    o_ref, lse_ref = oracle.attention_fp8_ref(x.q_bits, x.k_bits, x.v_bits, 1.0, 1.0, 1.0, scale,
+                                              causal)
+    _check("far rescale", o, lse, o_ref, lse_ref,
+           *_bounds(qv, kv, vv, scale, causal, o_ref, lse_ref, False))
+
+
+def test_fp8_score_accumulation_within_eps():
+    """The fp8 matrix instruction's accumulation error, seen through the
+    scores: with one key, LSE = scale q.k as the kernel sums it (a weight
+    sum of exactly one block-scaled 2^8), so |LSE - scale q.k| bounds that
+    instruction's error on each row's 128 products. It must stay within
+    eps = 2^-10 of |scale| sum_k |q_k k_k| (plus float32 rounding of the
+    final products). Rows: one 448 and seven 2^-9 in every group of 8
+    products at each position of the large term, mixed signs, and
+    amax-scaled normal codes; head 0's key is all ones, head 1's random."""
+    say("[case] fp8 score accumulation against eps = 2^-10")
+    d, nq = 128, 512
+    rng = np.random.default_rng(515)
+    rows = []
+    for pos in range(8):                       # large product at each group position
+        r = np.full(d, 2.0 ** -9)
+        r[pos::8] = 448.0
+        rows.append(r)
+        rows.append(r * np.where(rng.random(d) < 0.5, -1.0, 1.0))
+    while len(rows) < nq:
+        z = rng.standard_normal(d)
+        rows.append(oracle.e4m3_value(W.to_e4m3_bits((z * (448.0 / np.abs(z).max()))
+                                                      .astype(np.float32))))
+    qv = np.stack(rows)[None, :, None, :].repeat(2, axis=2)          # [1, nq, 2, d]
+    k_rand = oracle.e4m3_value(W.to_e4m3_bits((rng.standard_normal(d) * 16).astype(np.float32)))
+    kv = np.stack([np.ones(d), k_rand])[None, None]                   # [1, 1, 2, d]
+    x = W.Fp8Inputs(_codes(qv), _codes(kv), _codes(np.ones_like(kv)), 1.0, 1.0, 1.0)
+    scale = 1.0 / math.sqrt(d)
+    _, lse = _run(x, False, scale)
+    worst = 0.0
+    for h in range(2):
+        exact = scale * (qv[0, :, h] @ kv[0, 0, h])
+        absum = abs(scale) * (np.abs(qv[0, :, h]) @ np.abs(kv[0, 0, h]))
+        err = np.abs(lse[0, h] - exact)
+        assert np.all(err <= EPS * absum + 1e-6 * np.abs(exact) + 1e-30), (
+            f"head {h}: worst err/(eps sum|ab|) {float((err / (EPS * absum)).max()):.3f}")
+        worst = max(worst, float((err / absum).max()))
+    say(f"[fp8 accumulation] largest error / sum|a b| = 2^{math.log2(max(worst, 1e-300)):.1f}")

@@ -18,7 +18,8 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_parity, pick_rows, run_gpu, say, to_device
+from gpu_util import (assert_parity, gather_picks, oracle_sequence, pick_rows, run_gpu, say,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,15 +103,16 @@ def test_workload2_full():
     assert_parity(o, lse, o_ref, lse_ref, "bf16", "workload 2")
 
 
-def _sampled(wid, n_random):
+def _run_nan_filled(wid):
+    """Workload ``wid`` through fa_fwd into NaN-filled O and LSE (a row the
+    kernel fails to write stays NaN). Returns (inputs, O, LSE) as torch
+    device tensors after checking every output is finite."""
     import torch
 
     import exact_io_aware_63_amd as fa
     w = W.WORKLOADS[wid]
-    say(f"[case] workload {wid}: {w.name} (sampled rows)")
     inp = W.draw_workload(wid)
     q, k, v, cu = to_device(inp)
-    # NaN-filled outputs: a row the kernel fails to write stays NaN
     o0 = torch.full_like(q, float("nan"))
     l0 = torch.full((w.hq, q.shape[0]) if cu is not None else (q.shape[0], w.hq, q.shape[1]),
                     float("nan"), dtype=torch.float32, device=q.device)
@@ -118,33 +120,48 @@ def _sampled(wid, n_random):
                               max_seqlen=inp.max_seqlen if cu is not None else None,
                               out=o0, lse=l0)
     torch.cuda.synchronize()
-    picks = pick_rows(inp, n_random, seed=wid, hq=w.hq)
-    pt = torch.from_numpy(picks).to(o.device)
-    if cu is None:
-        og = o[pt[:, 0], pt[:, 2], pt[:, 1]]
-        lg = lse[pt[:, 0], pt[:, 1], pt[:, 2]]
-    else:
-        tok = cu.long()[pt[:, 0]] + pt[:, 2]
-        og = o[tok, pt[:, 1]]
-        lg = lse[pt[:, 1], tok]
-    og = og.float().cpu().double().numpy()
-    lg = lg.cpu().double().numpy()
-    assert np.all(np.isfinite(og)), "non-finite outputs"
-    o_ref, lse_ref = oracle.attention_picked(inp.q, inp.k, inp.v, w.scale, w.causal, picks,
-                                             cu_seqlens=inp.cu_seqlens)
-    assert_parity(og, lg, o_ref, lse_ref, "bf16", f"workload {wid} ({len(picks)} rows)")
     # every row written (the NaN fill is gone) and finite
     assert bool(torch.isfinite(o.float()).all()), "O has non-finite values"
     assert bool(torch.isfinite(lse).all()), "LSE has non-finite values"
+    return inp, o, lse
 
 
-def test_workload3_sampled():
-    _sampled(3, 384)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid", [3, 4])
+def test_workload_full(wid):
+    """Causal bf16 workloads at full size (32 heads, N = 4096 or 8192 with
+    GQA 32/8, d = 128): every element of O and LSE against the whole fp64
+    oracle."""
+    w = W.WORKLOADS[wid]
+    say(f"[case] workload {wid}: {w.name} (every element)")
+    inp, o, lse = _run_nan_filled(wid)
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    assert inp.q.shape[0] == 1
+    o_ref, lse_ref = oracle_sequence(inp.q[0], inp.k[0], inp.v[0], w.scale, w.causal)
+    assert_parity(o[0], lse[0], o_ref, lse_ref, "bf16", f"workload {wid} (all {o.size} values)")
 
 
-def test_workload4_sampled():
-    _sampled(4, 384)
-
-
-def test_workload5_sampled():
-    _sampled(5, 512)
+@pytest.mark.timeout(900)
+def test_workload5_shortest_longest_and_sampled():
+    """Packed variable-length workload: every row of the shortest and of the
+    longest sequence for all heads against the whole fp64 oracle of that
+    sequence, plus sampled rows (edges and random) of every sequence."""
+    w = W.WORKLOADS[5]
+    say(f"[case] workload 5: {w.name} (shortest + longest sequence, sampled rows)")
+    inp, o, lse = _run_nan_filled(5)
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    lens = np.asarray(inp.lens, dtype=np.int64)
+    cu = inp.cu_seqlens.astype(np.int64)
+    for s in sorted({int(np.argmin(lens)), int(np.argmax(lens))}):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        o_ref, lse_ref = oracle_sequence(inp.q[lo:hi], inp.k[lo:hi], inp.v[lo:hi], w.scale,
+                                         w.causal)
+        assert_parity(o[lo:hi], lse[:, lo:hi], o_ref, lse_ref, "bf16",
+                      f"workload 5 sequence {s} (length {hi - lo}, all heads)")
+    picks = pick_rows(inp, 512, seed=5, hq=w.hq)
+    og, lg = gather_picks(o, lse, picks, inp)
+    o_ref, lse_ref = oracle.attention_picked(inp.q, inp.k, inp.v, w.scale, w.causal, picks,
+                                             cu_seqlens=inp.cu_seqlens)
+    assert_parity(og, lg, o_ref, lse_ref, "bf16", f"workload 5 ({len(picks)} sampled rows)")
