@@ -5,7 +5,8 @@ HIP kernels behind the C ABI in ``include/fa.h``. PyTorch supplies device
 memory and the stream; the library calls no torch operation.
 
 The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_fwd_window``, ``fa_fwd_bias``,
-``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``, ``fa_fwd_fp8``,
+``fa_bwd``, ``fa_bwd_window``, ``fa_bwd_bias``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_noalloc``, ``fa_fwd_fp8``,
 ``fa_check_cu_seqlens``, ``fa_status_string``,
 ``fa_last_error`` and ``fa_version`` mirror the C entry points one to one
 (raw integers and device addresses). ``attention_fwd`` is a convenience
@@ -72,6 +73,10 @@ _lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
                                 [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
 _lib.fa_fwd_splitkv.restype = ctypes.c_int
+_lib.fa_fwd_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p])
+_lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
 _lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float] * 4 +
                             [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
 _lib.fa_fwd_fp8.restype = ctypes.c_int
@@ -90,7 +95,8 @@ _lib.fa_version.restype = ctypes.c_int
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
             "fa_bwd_bias",
-            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_fp8",
+            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_noalloc",
+            "fa_fwd_fp8",
             "fa_fwd_fp8_workspace_bytes", "fa_check_cu_seqlens", "fa_status_string",
             "fa_last_error", "fa_version")
 
@@ -160,6 +166,17 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlen
     """C ``fa_fwd_splitkv``: pointers are integer device addresses (or 0 / None)."""
     return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
                                seqlens_k, num_splits, workspace, workspace_bytes, stream)
+
+
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k,
+                           num_splits, stream) -> int:
+    """C ``fa_fwd_splitkv_noalloc``: pointers are integer device addresses
+    (or 0 / None); the split scratch is the library's own per-GPU array."""
+    return _lib.fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                                       int(causal), seqlens_k, num_splits, stream)
 
 
 def fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:

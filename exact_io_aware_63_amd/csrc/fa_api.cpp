@@ -327,9 +327,12 @@ size_t decode_workspace(int B, int Hq, int Nq, int d, int n_splits) {
   return ((o_bytes + 255) / 256) * 256 + rows * 4;
 }
 
+// use_scratch: the library's own device array takes the place of the
+// workspace (fa_fwd_splitkv_noalloc); `workspace` is then ignored.
 int run_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
                 int Hkv, int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
-                int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                int n_splits, void* workspace, size_t workspace_bytes, void* stream,
+                bool use_scratch = false) {
   g_last_error[0] = '\0';
   if (B < 0 || Nq < 0 || Nk < 0)
     return fail(FA_ERR_SHAPE, "B=%d, Nq=%d, Nk=%d must be >= 0", B, Nq, Nk);
@@ -345,20 +348,30 @@ int run_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE
     return fail(FA_ERR_ARG, "num_splits=%d must be in 1..%d", n_splits, kMaxSplits);
   if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale is not finite");
   if (B == 0 || Nq == 0) return FA_OK;
-  if (!Q || !O || !LSE || !workspace || (Nk > 0 && (!K || !V)))
+  if (!Q || !O || !LSE || (!use_scratch && !workspace) || (Nk > 0 && (!K || !V)))
     return fail(FA_ERR_NULL, "Q, O, LSE, workspace (and K, V when Nk > 0) must be non-NULL");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-      !aligned(workspace, 256))
+      (!use_scratch && !aligned(workspace, 256)))
     return fail(FA_ERR_ARG, "Q, K, V and O must be 16-byte aligned, workspace 256-byte aligned");
   if (!aligned(LSE, 4) || (seqlens_k && !aligned(seqlens_k, 4)))
     return fail(FA_ERR_ARG, "LSE and seqlens_k must be 4-byte aligned");
   const size_t need = decode_workspace(B, Hq, Nq, d, n_splits);
-  if (workspace_bytes < need)
+  if (use_scratch && need > fa::kNoAllocScratchBytes)
+    return fail(FA_ERR_ARG,
+                "the call needs %zu bytes of split scratch; fa_fwd_splitkv_noalloc holds %zu "
+                "(fewer splits or a smaller batch, or fa_fwd_splitkv with a workspace)",
+                need, fa::kNoAllocScratchBytes);
+  if (!use_scratch && workspace_bytes < need)
     return fail(FA_ERR_ARG, "workspace of %zu bytes; %zu needed", workspace_bytes, need);
   if (static_cast<long>(B) * Hkv * n_splits > 0x7fffffffL)
     return fail(FA_ERR_SHAPE, "grid exceeds the launch limit");
   int st = check_device();
   if (st != FA_OK) return st;
+  if (use_scratch) {
+    const hipError_t se = fa::decode_scratch(&workspace);
+    if (se != hipSuccess)
+      return fail(FA_ERR_HIP, "looking up the scratch array failed: %s", hipGetErrorString(se));
+  }
   fa::DecodeParams p;
   p.q = Q;
   p.k = K;
@@ -517,6 +530,15 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    size_t workspace_bytes, void* stream) {
   return run_splitkv(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k, num_splits,
                      workspace, workspace_bytes, stream);
+}
+
+static_assert(FA_NOALLOC_SCRATCH_BYTES == fa::kNoAllocScratchBytes, "scratch size in the header");
+
+int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                           const int32_t* seqlens_k, int num_splits, void* stream) {
+  return run_splitkv(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, d, scale, causal, seqlens_k, num_splits,
+                     nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Nk) {

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <mutex>
 
 #include "fa_bf16_common.h"
 #include "fa_launch.h"
@@ -283,5 +284,37 @@ hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
 
 template hipError_t launch_decode_bf16<64>(const DecodeParams&, hipStream_t);
 template hipError_t launch_decode_bf16<128>(const DecodeParams&, hipStream_t);
+
+// Partial O and LSE of every split for fa_fwd_splitkv_noalloc. Each GPU
+// that loads the library holds its own copy until the process ends; every
+// call on a GPU reuses it (the split pass writes every partial row that the
+// combine pass reads, so nothing needs clearing between calls).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  // in host code `scratch` names a host-side stand-in: only the address the
+  // runtime reports for the current device may reach a kernel
+  std::call_once(slot.once, [&] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+  });
+  if (slot.err != hipSuccess) return slot.err;
+  *ptr = slot.ptr;
+  return hipSuccess;
+}
 
 }  // namespace fa

@@ -109,6 +109,14 @@ hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 extern template hipError_t launch_decode_bf16<64>(const DecodeParams&, hipStream_t);
 extern template hipError_t launch_decode_bf16<128>(const DecodeParams&, hipStream_t);
 
+// Scratch of fa_fwd_splitkv_noalloc: a file-scope device array of this many
+// bytes in fa_decode_bf16.hip takes the place of the caller's workspace.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+
+// Device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call for each device (thread-safe).
+hipError_t decode_scratch(void** ptr);
+
 // One FP8 (e4m3) attention-forward problem, already validated on the host:
 // fixed length, d = 128, Q [B, Nq, Hq, 128], K and V [B, Nk, Hkv, 128]
 // (bytes), O [B, Nq, Hq, 128] bf16, LSE [B, Hq, Nq].

@@ -243,6 +243,26 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O,
                    void* stream);
 
 /*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The partial results live in a
+ * device array the library holds, FA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU
+ * for the life of the process; a call whose
+ * fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) exceeds that
+ * fails with FA_ERR_ARG before any HIP call. The call allocates nothing.
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (different streams, or threads without ordering) race and their
+ * results are undefined; calls ordered on one stream are safe. Other
+ * arguments, results and errors as fa_fwd_splitkv.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O,
+                           float* LSE, int B, int Hq, int Hkv, int Nq, int Nk,
+                           int d, float scale, int causal,
+                           const int32_t* seqlens_k, int num_splits,
+                           void* stream);
+
+/*
  * Attention forward with FP8 inputs: Q, K, V in OCP e4m3 (1 sign, 4
  * exponent bits with bias 7, 3 mantissa bits; no infinities, 0x7f / 0xff
  * are NaN) with one dequantization factor per tensor. The function is the

@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
          "fa_bwd_bias", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes",
-         "fa_fwd_splitkv_workspace_bytes", "fa_check_cu_seqlens",
+         "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_noalloc", "fa_check_cu_seqlens",
          "fa_status_string", "fa_last_error", "fa_version"])
 
 
@@ -457,3 +457,36 @@ def test_check_cu_seqlens_null_and_negative(fa):
     assert fa.fa_check_cu_seqlens(None, 2, 8) == fa.FA_ERR_NULL
     assert fa.fa_check_cu_seqlens(None, 0, 8) == fa.FA_OK
     assert fa.fa_check_cu_seqlens(None, -1, 8) == fa.FA_ERR_SHAPE
+
+
+def _call_noalloc(fa, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nq=1, Nk=300, d=128, scale=0.1,
+             causal=0, lens=None, splits=4, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                     a["lens"], a["splits"], a["stream"])
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(fa):
+    """The allocation-free entry point refuses, on the host, any call whose
+    split scratch exceeds the fixed array; just below the limit it passes
+    the host checks (and stops at the device check without a GPU)."""
+    import torch
+    lim = fa.FA_NOALLOC_SCRATCH_BYTES
+    # B * Hq * Nq * splits rows of (d + 1) floats, the O part padded to 256 B
+    big = dict(B=64, Hq=32, Hkv=8, Nq=1, splits=64)
+    assert fa.fa_fwd_splitkv_workspace_bytes(64, 32, 1, 128, 64) > lim
+    assert _call_noalloc(fa, **big) == fa.FA_ERR_ARG
+    assert "scratch" in fa.fa_last_error()
+    ok = dict(B=64, Hq=32, Hkv=8, Nq=1, splits=15)
+    assert fa.fa_fwd_splitkv_workspace_bytes(64, 32, 1, 128, 15) <= lim
+    if not torch.cuda.is_available():
+        assert _call_noalloc(fa, **ok) == fa.FA_ERR_HIP
+
+
+@pytest.mark.parametrize("kw,status", [(dict(q=0), -1), (dict(splits=0), -4), (dict(d=96), -3),
+                                       (dict(Hq=6, Hkv=4), -2), (dict(Nq=9), -3),
+                                       (dict(B=0), 0), (dict(Nq=0), 0)])
+def test_noalloc_shares_the_host_checks(fa, kw, status):
+    assert _call_noalloc(fa, **kw) == status, fa.fa_last_error()
