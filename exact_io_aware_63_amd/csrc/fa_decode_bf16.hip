@@ -15,12 +15,15 @@
 //
 // Query rows: the Hq/Hkv query heads that share K/V head g, times Nq rows,
 // form one 32-row query tile (row r = group head r / Nq, query r % Nq), so
-// one pass over the K/V tiles serves the whole group. All four waves of a
-// workgroup form the same scores S^T = K Q^T (lane = query row, registers =
-// keys) and the same online state (m, l); wave w accumulates output columns
-// 32w .. 32w+31 (d = 128) of O^T += V^T P^T, so no state is merged across
-// waves. The problem is bound by HBM reads of K and V; the repeated score
-// MFMAs cost matrix-core time that is otherwise idle.
+// one pass over the K/V tiles serves the whole group. One wavefront per
+// workgroup owns one (batch entry, K/V head, key range): it forms the scores
+// S^T = K Q^T of 32 keys at a time (lane = query row, registers = keys),
+// keeps the online state (m, l) and accumulates all of O^T += V^T P^T, so
+// no state is merged inside a workgroup and no key is scored twice. The
+// problem is bound by HBM reads of K and V: each wave keeps the next stage's
+// loads in flight while it computes, the loads bypass reuse in the caches
+// (each K/V byte is read once), and small per-wave LDS rings let five waves
+// share a compute unit.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -66,31 +69,70 @@ __device__ __forceinline__ bf16x8 row_operand_dec(const unsigned char* tile, int
   return *reinterpret_cast<const bf16x8*>(tile + row * T::kRowBytes + unit * 16);
 }
 
+// One wavefront per workgroup: it streams its own key range through a ring
+// of kDecStages LDS slots of kDecKeys keys (K and V), filled by
+// buffer-to-LDS loads that no other wave touches, so the ring needs no
+// barrier, only the wave's own count of loads in flight.
+constexpr int kDecKeys = 32;    // keys per stage (one 32x32 score tile)
+constexpr int kDecStages = 2;   // ring slots: one stage in flight while one is read
+constexpr int kDecThreads = 64;
+constexpr int kDecLoadAux = 2;  // cache policy of the K/V loads: non-temporal (read once)
+
+template <int D>
+struct DecStage {
+  static constexpr int kUnits = D / 8;                        // 16-byte units per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kDecKeys * kRowBytes;         // one tensor of one stage
+  static constexpr int kLoads = kDecKeys * kUnits / kDecThreads;  // 16-byte loads per lane
+};
+
 // Keys [kbeg, kend) of split s of a sequence with Lk keys: equal ranges,
-// rounded up to whole 64-key tiles.
+// rounded up to whole stages.
 __device__ __forceinline__ void split_range(int Lk, int n_splits, int s, int& kbeg, int& kend) {
-  const int per = ((Lk + n_splits - 1) / n_splits + kTileRows - 1) / kTileRows * kTileRows;
+  const int per = ((Lk + n_splits - 1) / n_splits + kDecKeys - 1) / kDecKeys * kDecKeys;
   kbeg = min(Lk, s * per);
   kend = min(Lk, kbeg + per);
 }
 
+// Loads of keys r0 .. r0+31 of one tensor into an LDS slot, in the
+// swizzled row layout the operand reads expect; keys at or past kend lie
+// outside the buffer range and arrive as zeros.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-  using T = Tile<D>;
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;  // d-tiles of O^T; waves >= ND idle in the P V product
-  // Two slots per tensor as separate arrays, chosen at compile time (the
-  // loop is unrolled by two): with one array indexed at run time the
-  // compiler cannot tell the slot being loaded from the slot being read,
-  // and waits for the new tile's loads before every read of the current one.
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[T::kBytes];
+__device__ __forceinline__ void issue_stage(const u16* g, uint32_t stride_b, int r0, int kend,
+                                            unsigned char* dst, int lane) {
+  using T = DecStage<D>;
+  const int rows = min(kend - r0, kDecKeys);
+  const uint32_t nrec = static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g + static_cast<long>(r0) * (stride_b / 2)), 0, nrec, kBufferFlags);
+#pragma unroll
+  for (int it = 0; it < T::kLoads; ++it) {
+    const int u = it * kDecThreads + lane;
+    const int row = u / T::kUnits;
+    const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + it * kDecThreads * 16), 16,
+                                             row * stride_b + gc * 16, 0, 0, kDecLoadAux);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Wait until at most n stages (2 * kLoads loads each) are still in flight.
+template <int D>
+__device__ __forceinline__ void wait_stages(int n) {
+  constexpr int L = 2 * DecStage<D>::kLoads;
+  if (n >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * L) : "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(L) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+static_assert(kDecStages >= 2 && kDecStages <= 4, "wait_stages covers up to two newer stages");
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams p) {
+  using T = DecStage<D>;
+  constexpr int NC = D / 16;  // 16-wide d chunks of the score contraction
+  constexpr int ND = D / 32;  // 32-row d tiles of O^T
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecStages][2][T::kBytes];
+
+  const int lane = threadIdx.x;
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
@@ -112,10 +154,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 
   const long qstride = static_cast<long>(p.hq) * D;
   const long kstride = static_cast<long>(p.hkv) * D;
+  const uint32_t stride_b = static_cast<uint32_t>(kstride * 2);
   const u16* kg = static_cast<const u16*>(p.k) + static_cast<long>(b) * p.nk * kstride +
                   static_cast<long>(kvh) * D;
   const u16* vg = static_cast<const u16*>(p.v) + static_cast<long>(b) * p.nk * kstride +
                   static_cast<long>(kvh) * D;
+
+  const int nst = (kend - kbeg + kDecKeys - 1) / kDecKeys;  // stages of this split
+  auto issue = [&](int s) {
+    unsigned char* slot = &ring[s % kDecStages][0][0];
+    issue_stage<D>(kg, stride_b, kbeg + s * kDecKeys, kend, slot, lane);
+    issue_stage<D>(vg, stride_b, kbeg + s * kDecKeys, kend, slot + T::kBytes, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < kDecStages - 1; ++s)
+    if (s < nst) issue(s);
 
   bf16x8 qf[NC];
 #pragma unroll
@@ -129,76 +182,54 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const float c = p.scale_log2;
   float m = -INFINITY;  // running max of c * s (base 2)
   float l = 0.f;        // this lane's part of the denominator
-  f32x16 acc = f32x16{};
+  f32x16 acc[ND];
+#pragma unroll
+  for (int t = 0; t < ND; ++t) acc[t] = f32x16{};
 
-  const int nkb = (kend - kbeg + kTileRows - 1) / kTileRows;
-  if (nkb > 0) {
-    issue_tile<D>(kg, kstride, kbeg, kend, k_st0, tid, w);
-    issue_tile<D>(vg, kstride, kbeg, kend, v_st0, tid, w);
-  }
-  auto step = [&](auto par_tag, int it) {
-    constexpr int PAR = decltype(par_tag)::value;  // it & 1
-    const unsigned char* k_cur = PAR ? k_st1 : k_st0;
-    const unsigned char* v_cur = PAR ? v_st1 : v_st0;
-    unsigned char* k_nxt = PAR ? k_st0 : k_st1;
-    unsigned char* v_nxt = PAR ? v_st0 : v_st1;
-    const int k0 = kbeg + it * kTileRows;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (it + 1 < nkb) {
-      issue_tile<D>(kg, kstride, k0 + kTileRows, kend, k_nxt, tid, w);
-      issue_tile<D>(vg, kstride, k0 + kTileRows, kend, v_nxt, tid, w);
+  for (int s = 0; s < nst; ++s) {
+    // stage s has landed once at most the stages issued after it remain
+    wait_stages<D>(min(kDecStages - 2, nst - 1 - s));
+    // the slot read in the previous iteration is free: refill it
+    if (s + kDecStages - 1 < nst) issue(s + kDecStages - 1);
+    const unsigned char* kst = &ring[s % kDecStages][0][0];
+    const unsigned char* vst = kst + T::kBytes;
+    const int ks0 = kbeg + s * kDecKeys;
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand_dec<D>(kst, 0, cc, lane), qf[cc],
+                                                   st, 0, 0, 0);
+    // x = c * s on visible keys, -inf elsewhere
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = ks0 + drow(r, h2);
+      const bool vis = key < kend && (!p.causal || key <= qi);
+      st[r] = vis ? st[r] * c : -INFINITY;
+      mx = fmaxf(mx, st[r]);
     }
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float ref = m_new == -INFINITY ? 0.f : m_new;  // a row with no visible key yet
+    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    m = m_new;
+    float rs = 0.f;
+    bf16x8 pb[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int ks0 = k0 + 32 * sub;
-      if (ks0 >= kend) break;
-      f32x16 st = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand_dec<D>(k_cur, 32 * sub, cc, lane),
-                                                     qf[cc], st, 0, 0, 0);
-      // x = c * s on visible keys, -inf elsewhere
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = ks0 + drow(r, h2);
-        const bool vis = key < kend && (!p.causal || key <= qi);
-        st[r] = vis ? st[r] * c : -INFINITY;
-        mx = fmaxf(mx, st[r]);
-      }
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float ref = m_new == -INFINITY ? 0.f : m_new;  // a row with no visible key yet
-      const float alpha = __builtin_amdgcn_exp2f(m - ref);
-      m = m_new;
-      f32x16 pr;
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(st[r] - ref);
-        rs += pr[r];
-      }
-      l = l * alpha + rs;
-      if (w < ND) {
-        acc *= alpha;
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          bf16x8 pb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(pr[8 * g + i]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand_dec<D>(v_cur, 32 * sub, w, g, lane),
-                                                        pb, acc, 0, 0, 0);
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float x = __builtin_amdgcn_exp2f(st[r] - ref);
+      rs += x;
+      pb[r >> 3][r & 7] = static_cast<__bf16>(x);
     }
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  for (int it = 0; it < nkb; it += 2) {
-    step(P0{}, it);
-    if (it + 1 >= nkb) break;
-    step(P1{}, it + 1);
+    l = l * alpha + rs;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      acc[t] *= alpha;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand_dec<D>(vst, 0, t, g, lane),
+                                                         pb[g], acc[t], 0, 0, 0);
+    }
   }
 
   // Partial results of this split: o_s = a / l (float32) and LSE_s (natural
@@ -206,27 +237,40 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const float l_tot = xhalf_sum(l);
   if (row_ok) {
     const long prow = ((static_cast<long>(split) * p.batch + b) * p.hq + h) * p.nq + qi;
-    if (w < ND) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* og = p.part_o + prow * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* og = p.part_o + prow * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         float4 o4;
-        o4.x = acc[4 * g4 + 0] * inv;
-        o4.y = acc[4 * g4 + 1] * inv;
-        o4.z = acc[4 * g4 + 2] * inv;
-        o4.w = acc[4 * g4 + 3] * inv;
-        *reinterpret_cast<float4*>(og + 32 * w + 8 * g4 + 4 * h2) = o4;
+        o4.x = acc[t][4 * g4 + 0] * inv;
+        o4.y = acc[t][4 * g4 + 1] * inv;
+        o4.z = acc[t][4 * g4 + 2] * inv;
+        o4.w = acc[t][4 * g4 + 3] * inv;
+        *reinterpret_cast<float4*>(og + 32 * t + 8 * g4 + 4 * h2) = o4;
       }
-    }
-    if (w == 0 && h2 == 0)
-      p.part_lse[prow] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2d : -INFINITY;
+    if (h2 == 0) p.part_lse[prow] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2d : -INFINITY;
   }
 }
 
 // Merge the splits of one (batch entry, q-head, query row) per wave: the
 // row's LSE = log sum_s exp(LSE_s) and o = sum_s exp(LSE_s - LSE) o_s, then
-// o rounded once to bf16. A row no split sees gets o = 0, LSE = -inf.
+// o rounded once to bf16. A row no split sees gets o = 0, LSE = -inf. Lane
+// s holds split s's LSE and weight (64 splits at a time), so the maximum
+// and the weight sum are wave reductions and the partial rows' loads do not
+// wait on each other.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
   const long row = static_cast<long>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
@@ -234,23 +278,50 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
   const long n_rows = static_cast<long>(p.batch) * p.hq * p.nq;
   if (row >= n_rows) return;
   const long split_stride = n_rows;  // part rows of consecutive splits
+  const int ns = p.n_splits;
   float mx = -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) mx = fmaxf(mx, p.part_lse[s * split_stride + row]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) mx = fmaxf(mx, p.part_lse[(s0 + lane) * split_stride + row]);
+  mx = wave_max(mx);
   float o[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float sum = 0.f;
-    for (int s = 0; s < p.n_splits; ++s) {
-      const float ls = p.part_lse[s * split_stride + row];
-      if (ls == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f((ls - mx) * kLog2ed);
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      // this lane's split weight (0 for a split that saw no key)
+      float wgt = 0.f;
+      if (s0 + lane < ns) {
+        const float ls = p.part_lse[(s0 + lane) * split_stride + row];
+        wgt = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ls - mx) * kLog2ed);
+      }
       sum += wgt;
-      const float* src = p.part_o + (s * split_stride + row) * D;
+      const int n = min(64, ns - s0);
+      int s = 0;
+      for (; s + 4 <= n; s += 4) {  // four partial rows in flight
+        float src[4][D / 64];
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) o[e] = __builtin_fmaf(wgt, src[e * 64 + lane], o[e]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e)
+            src[u][e] = p.part_o[((s0 + s + u) * split_stride + row) * D + e * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wu = __shfl(wgt, s + u);
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) o[e] = __builtin_fmaf(wu, src[u][e], o[e]);
+        }
+      }
+      for (; s < n; ++s) {
+        const float wu = __shfl(wgt, s);
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e)
+          o[e] = __builtin_fmaf(wu, p.part_o[((s0 + s) * split_stride + row) * D + e * 64 + lane],
+                                o[e]);
+      }
     }
+    sum = wave_sum(sum);
     const float inv = 1.f / sum;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) o[e] *= inv;
@@ -273,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
 template <int D>
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.batch) * p.hkv * p.n_splits;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(grid), dim3(kDecThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long n_rows = static_cast<long>(p.batch) * p.hq * p.nq;
