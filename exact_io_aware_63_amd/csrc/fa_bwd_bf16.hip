@@ -102,6 +102,11 @@ __device__ __forceinline__ bf16x8 pack_chunk(const f32x16& x, int g) {
   return r;
 }
 
+// Component i (a compile-time constant after unrolling) of a float4.
+__device__ __forceinline__ float f4_at(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 // Key `key` visible to query `q` (sequence-local): inside both sequences,
 // under the causal mask, and inside the sliding window when WIN.
 template <bool CAUSAL, bool WIN>
@@ -194,6 +199,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dot_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
+
+// Score MFMAs for the interleaved plan below: as mfma_qk_first/acc, with
+// two wait states first, because vector instructions now sit right before
+// them and the compiler does not see the asm as a matrix instruction (a
+// vector write of an operand register needs two wait states before an MFMA
+// reads it).
+__device__ __forceinline__ f32x16 mfma_qk_first_w(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk_acc_w(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
 
 // Exponent offset of a row: -LSE in base 2, or -inf for a row with
 // LSE = -inf when a bias is present (its pairs may be visible with B = -inf,
@@ -323,16 +342,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
     const unsigned char* ds_ = PAR ? do_st1 : do_st0;
     const float* ls = PAR ? lse_st1 : lse_st0;
     const float* dsm = PAR ? d_st1 : d_st0;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    // Sub-block `sub` alone: scores, then its vector work, then its
+    // products (the biased kernels).
+    auto serial_item = [&](int sub) {
       const int r0 = 32 * sub;  // tile row of this 32-row sub-block
       const int qs0 = q0 + r0;  // its first query
-      if (qs0 >= sb.Lq) break;
-      if (CAUSAL && qs0 + 31 < kw0) continue;  // every query before every key of the wave
-      if constexpr (WIN) {  // every query outside every window of the wave's keys
-        if (p.win_right >= 0 && qs0 + 31 < kw0 - p.win_right) continue;
-        if (p.win_left >= 0 && qs0 > kw0 + 31 + p.win_left) continue;
-      }
       // Bias of this lane's key against the block's 16 queries of this
       // half-wave (indices clamped into the sequence; clamped values belong
       // to invisible pairs and are never used).
@@ -399,6 +413,169 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
           asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
         }
       }
+    };
+    // Is sub-block `sub` of this tile active for this wave (rows in the
+    // sequence, some pair possibly visible)?
+    auto active = [&](int sub) {
+      const int qs0 = q0 + 32 * sub;
+      if (qs0 >= sb.Lq) return false;
+      if (CAUSAL && qs0 + 31 < kw0) return false;  // every query before every key of the wave
+      if constexpr (WIN) {  // every query outside every window of the wave's keys
+        if (p.win_right >= 0 && qs0 + 31 < kw0 - p.win_right) return false;
+        if (p.win_left >= 0 && qs0 > kw0 + 31 + p.win_left) return false;
+      }
+      return true;
+    };
+    // every pair of sub-block `sub` exists and is visible: no per-element test
+    auto all_visible = [&](int sub) {
+      const int qs0 = q0 + 32 * sub;
+      return !WIN && qs0 + 31 < sb.Lq && kw0 + 31 < sb.Lk && (!CAUSAL || qs0 >= kw0 + 31);
+    };
+    // P and dS of register r of a sub-block, in place (s becomes P, dp
+    // becomes dS), from the row's LSE and D (lv, dvv). No mask here: masked
+    // tiles are cleared afterwards by mask_sub.
+    auto prob_elem = [&](int r, f32x16& sv, f32x16& dpv, float lv, float dvv) {
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, neg_lse2<false>(lv)));
+      const float dd = dpv[r] - dvv;
+      sv[r] = pe;
+      dpv[r] = pe * dd;
+    };
+    // Zero P and dS of the invisible pairs of sub-block `sub` (a select, so
+    // whatever the exponential gave for such a pair, inf included, is gone).
+    auto mask_sub = [&](int sub, f32x16& pv, f32x16& dsv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = visible<CAUSAL, WIN>(p, q0 + 32 * sub + mrow(r, h2), key, sb.Lq, sb.Lk);
+        pv[r] = vis ? pv[r] : 0.f;
+        dsv[r] = vis ? dsv[r] : 0.f;
+      }
+    };
+    // Both sub-blocks active: a software pipeline over the tile. The matrix
+    // cores form the second sub-block's S and dP while the vector unit turns
+    // the first one's scores into P and dS, then accumulate the first one's
+    // dV and dK while the vector unit does the second one's; one MFMA per
+    // step, the vector work spread evenly over the steps.
+    auto pipelined = [&](bool full0, bool full1) {
+      constexpr int NS = 2 * NC;        // score steps: S and dP chains interleaved
+      constexpr int NP = 4 * ND;        // product steps: 2 chunks x ND tiles x (dV, dK)
+      constexpr int EPS = 16 / NS;      // elements per score step
+      constexpr int EPP = 16 / NP;      // elements per product step
+      static_assert(EPS * NS == 16 && EPP * NP == 16, "element spread");
+      // LSE and D of a sub-block's rows: registers 4g4 .. 4g4+3 are rows
+      // 32*sub + 8g4 + 4*h2 + (0..3); each group is read two steps before
+      // its first element
+      float4 l4[4], d4[4];
+      auto load_ld = [&](int sub, int g4) {
+        l4[g4] = *reinterpret_cast<const float4*>(ls + 32 * sub + 8 * g4 + 4 * h2);
+        d4[g4] = *reinterpret_cast<const float4*>(dsm + 32 * sub + 8 * g4 + 4 * h2);
+      };
+      load_ld(0, 0);
+      // phase 1: S and dP of sub-block 0
+      f32x16 s0 = mfma_qk_first(row_operand<D>(qs, 0, 0, lane), kf[0]);
+      f32x16 p0 = mfma_qk_first(row_operand<D>(ds_, 0, 0, lane), vf[0]);
+#pragma unroll
+      for (int cc = 1; cc < NC; ++cc) {
+        mfma_qk_acc(s0, row_operand<D>(qs, 0, cc, lane), kf[cc]);
+        mfma_qk_acc(p0, row_operand<D>(ds_, 0, cc, lane), vf[cc]);
+      }
+      mfma_result_guard();
+      // phase 2: S and dP of sub-block 1 on the matrix cores, P and dS of
+      // sub-block 0 on the vector unit. Operands are read two steps ahead.
+      f32x16 s1, p1;
+      bf16x8 op[NS];
+      auto load_op = [&](int k) {
+        op[k] = row_operand<D>((k & 1) ? ds_ : qs, 32, k >> 1, lane);
+      };
+      load_op(0);
+      load_op(1);
+      static_for<NS>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NS) load_op(k + 2);
+        static_for<3>([&](auto G) {  // groups 1..3
+          constexpr int g4 = decltype(G)::value + 1;
+          constexpr int at = (4 * g4) / EPS - 2;
+          if constexpr (at == k || (at < 0 && k == 0)) load_ld(0, g4);
+        });
+        constexpr int cc = k >> 1;
+        if constexpr ((k & 1) == 0) {
+          if constexpr (cc == 0) s1 = mfma_qk_first_w(op[k], kf[0]);
+          else mfma_qk_acc_w(s1, op[k], kf[cc]);
+        } else {
+          if constexpr (cc == 0) p1 = mfma_qk_first_w(op[k], vf[0]);
+          else mfma_qk_acc_w(p1, op[k], vf[cc]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          constexpr int r0e = k * EPS;
+          const int r = r0e + e;
+          prob_elem(r, s0, p0, f4_at(l4[r >> 2], r & 3), f4_at(d4[r >> 2], r & 3));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (!full0) mask_sub(0, s0, p0);
+      bf16x8 pb0[2], sbv0[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        pb0[g] = pack_chunk(s0, g);
+        sbv0[g] = pack_chunk(p0, g);
+      }
+      load_ld(1, 0);
+      mfma_result_guard();  // sub-block 1's chains finished before its vector work
+      // phase 3: dV and dK of sub-block 0 on the matrix cores, P and dS of
+      // sub-block 1 on the vector unit; transposed operands two steps ahead.
+      bf16x8 top[NP];
+      auto load_top = [&](int k) {
+        const int g = k / (2 * ND), t = (k >> 1) % ND;
+        top[k] = tr_operand<D>((k & 1) ? qs : ds_, 0, t, g, lane);
+      };
+      load_top(0);
+      load_top(1);
+      static_for<NP>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NP) load_top(k + 2);
+        static_for<3>([&](auto G) {
+          constexpr int g4 = decltype(G)::value + 1;
+          constexpr int at = (4 * g4) / EPP - 2;
+          if constexpr (at == k || (at < 0 && k == 0)) load_ld(1, g4);
+        });
+        constexpr int g = k / (2 * ND), t = (k >> 1) % ND;
+        if constexpr ((k & 1) == 0)
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[k], pb0[g], dv[t], 0, 0, 0);
+        else
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[k], sbv0[g], dk[t], 0, 0, 0);
+        asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+          const int r = k * EPP + e;
+          prob_elem(r, s1, p1, f4_at(l4[r >> 2], r & 3), f4_at(d4[r >> 2], r & 3));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // phase 4: dV and dK of sub-block 1
+      if (!full1) mask_sub(1, s1, p1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 pb = pack_chunk(s1, g);
+        const bf16x8 sbv = pack_chunk(p1, g);
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ds_, 32, t, g, lane), pb, dv[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, 32, t, g, lane), sbv, dk[t], 0, 0, 0);
+          asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
+        }
+      }
+    };
+    const bool act0 = active(0), act1 = active(1);
+    if constexpr (!BIAS) {
+      // An inactive sub-block of an active tile goes through the pipeline
+      // too, under the per-element test, so all its probabilities are 0
+      // (it happens only near the diagonal and at a ragged end).
+      if (act0 || act1) {
+        pipelined(act0 && all_visible(0), act1 && all_visible(1));
+      }
+    } else {
+      if (act0) serial_item(0);
+      if (act1) serial_item(1);
     }
   };
   {
@@ -542,16 +719,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
     }
     const unsigned char* ks = PAR ? k_st1 : k_st0;
     const unsigned char* vs = PAR ? v_st1 : v_st0;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    // Sub-block `sub` alone (the biased kernels): scores, then its vector
+    // work, then its product.
+    auto serial_item = [&](int sub) {
       const int r0 = 32 * sub;
       const int ks0 = key_base + kb * kTileRows + r0;  // first key of this 32-key sub-block
-      if (ks0 >= sb.Lk) break;
-      if (CAUSAL && ks0 > wq0 + 31) break;  // every key after every query of the wave
-      if constexpr (WIN) {  // every key outside every window of the wave's rows
-        if (p.win_right >= 0 && ks0 > wq0 + 31 + p.win_right) break;
-        if (p.win_left >= 0 && ks0 + 31 < wq0 - p.win_left) continue;
-      }
       // bias of keys ks0 + 8g + 4*h2 + (0..3) = registers 4g .. 4g+3
       u32x2 bias_v[4];
       if constexpr (BIAS) {
@@ -605,6 +777,114 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
           asm volatile("" : "+a"(dq[t]));
         }
       }
+    };
+    // Is 32-key sub-block `sub` of this tile active for this wave?
+    auto active = [&](int sub) {
+      const int ks0 = key_base + kb * kTileRows + 32 * sub;
+      if (ks0 >= sb.Lk) return false;
+      if (CAUSAL && ks0 > wq0 + 31) return false;  // every key after every query of the wave
+      if constexpr (WIN) {  // every key outside every window of the wave's rows
+        if (p.win_right >= 0 && ks0 > wq0 + 31 + p.win_right) return false;
+        if (p.win_left >= 0 && ks0 + 31 < wq0 - p.win_left) return false;
+      }
+      return true;
+    };
+    // every pair of sub-block `sub` exists and is visible
+    auto all_visible = [&](int sub) {
+      const int ks0 = key_base + kb * kTileRows + 32 * sub;
+      return !WIN && ks0 + 31 < sb.Lk && wq0 + 31 < sb.Lq && (!CAUSAL || ks0 + 31 <= wq0);
+    };
+    // dS^T of register r, in place into dpv: P (dP - D), P = 2^(c s - LSE)
+    auto dscore_elem = [&](int r, const f32x16& sv, f32x16& dpv) {
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, nlse2));
+      dpv[r] = pe * (dpv[r] - drow);
+    };
+    // zero dS^T of the invisible pairs of sub-block `sub` (a select)
+    auto mask_sub = [&](int sub, f32x16& dsv) {
+      const int ks0 = key_base + kb * kTileRows + 32 * sub;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dsv[r] = visible<CAUSAL, WIN>(p, qrow, ks0 + mrow(r, h2), sb.Lq, sb.Lk) ? dsv[r] : 0.f;
+    };
+    // Software pipeline over the tile's two sub-blocks (as in the dK/dV
+    // body): the second sub-block's S^T and dP^T chains run on the matrix
+    // cores while the vector unit forms the first one's dS^T, then the first
+    // one's dQ^T product runs while the vector unit does the second one's.
+    auto pipelined = [&](bool full0, bool full1) {
+      constexpr int NS = 2 * NC;   // score steps
+      constexpr int NP = 2 * ND;   // product steps: 2 chunks x ND tiles
+      constexpr int EPS = 16 / NS, EPP = 16 / NP;
+      static_assert(EPS * NS == 16 && EPP * NP == 16, "element spread");
+      // phase 1: S^T and dP^T of sub-block 0
+      f32x16 s0 = mfma_qk_first(row_operand<D>(ks, 0, 0, lane), qf[0]);
+      f32x16 p0 = mfma_qk_first(row_operand<D>(vs, 0, 0, lane), dof[0]);
+#pragma unroll
+      for (int cc = 1; cc < NC; ++cc) {
+        mfma_qk_acc(s0, row_operand<D>(ks, 0, cc, lane), qf[cc]);
+        mfma_qk_acc(p0, row_operand<D>(vs, 0, cc, lane), dof[cc]);
+      }
+      mfma_result_guard();
+      // phase 2: sub-block 1's chains with sub-block 0's dS^T
+      f32x16 s1, p1;
+      bf16x8 op[NS];
+      auto load_op = [&](int k) { op[k] = row_operand<D>((k & 1) ? vs : ks, 32, k >> 1, lane); };
+      load_op(0);
+      load_op(1);
+      static_for<NS>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NS) load_op(k + 2);
+        constexpr int cc = k >> 1;
+        if constexpr ((k & 1) == 0) {
+          if constexpr (cc == 0) s1 = mfma_qk_first_w(op[k], qf[0]);
+          else mfma_qk_acc_w(s1, op[k], qf[cc]);
+        } else {
+          if constexpr (cc == 0) p1 = mfma_qk_first_w(op[k], dof[0]);
+          else mfma_qk_acc_w(p1, op[k], dof[cc]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) dscore_elem(k * EPS + e, s0, p0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (!full0) mask_sub(0, p0);
+      bf16x8 sbv0[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) sbv0[g] = pack_chunk(p0, g);
+      mfma_result_guard();  // sub-block 1's chains finished before its vector work
+      // phase 3: sub-block 0's dQ^T product with sub-block 1's dS^T
+      bf16x8 top[NP];
+      auto load_top = [&](int k) { top[k] = tr_operand<D>(ks, 0, k % ND, k / ND, lane); };
+      load_top(0);
+      load_top(1);
+      static_for<NP>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NP) load_top(k + 2);
+        constexpr int g = k / ND, t = k % ND;
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top[k], sbv0[g], dq[t], 0, 0, 0);
+        asm volatile("" : "+a"(dq[t]));
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) dscore_elem(k * EPP + e, s1, p1);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // phase 4: sub-block 1's product
+      if (!full1) mask_sub(1, p1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 sbv = pack_chunk(p1, g);
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, 32, t, g, lane), sbv, dq[t], 0, 0, 0);
+          asm volatile("" : "+a"(dq[t]));
+        }
+      }
+    };
+    const bool act0 = active(0), act1 = active(1);
+    if constexpr (!BIAS) {
+      // inactive sub-blocks of an active tile go through the pipeline and
+      // are cleared by mask_sub
+      if (act0 || act1) pipelined(act0 && all_visible(0), act1 && all_visible(1));
+    } else {
+      if (act0) serial_item(0);
+      if (act1) serial_item(1);
     }
   };
   {
