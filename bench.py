@@ -223,6 +223,48 @@ def cpu_baseline(inp, w, budget_s: float = 12.0, do=None, bias_block=None, gpu_u
 
 
 # ---------------------------------------------------------------------------
+# Context: the materialising schedule on the same GPU
+# ---------------------------------------------------------------------------
+
+def standard_attention_ms(torch, q, k, v, w, stream, reps: int = 10):
+    """Time the standard three-pass schedule the pages contrast with the
+    tiled one (krlt.com Triptych day 39; "Understanding FlashAttention Pt 1",
+    section 1.2): S = scale Q K^T written to HBM, P = softmax(S) written to
+    HBM, O = P V, with torch on the GPU, all heads batched (K and V expanded
+    to the query heads beforehand, outside the timing). bf16 products, the
+    softmax in float32. Context only: this is not a path of the library."""
+    B, N, hq, d = q.shape
+    gq = w.hq // w.hkv
+    qh = q[0].transpose(0, 1).contiguous()                                  # [Hq, N, d]
+    kh = k[0].transpose(0, 1).repeat_interleave(gq, dim=0).contiguous()     # [Hq, N, d]
+    vh = v[0].transpose(0, 1).repeat_interleave(gq, dim=0).contiguous()
+    kt = kh.transpose(1, 2).contiguous()                                     # [Hq, d, N]
+    mask = torch.ones(N, N, dtype=torch.bool, device=q.device).triu_(1) if w.causal else None
+
+    def run():
+        s = torch.bmm(qh, kt).float().mul_(w.scale)
+        if mask is not None:
+            s.masked_fill_(mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).to(torch.bfloat16)
+        return torch.bmm(p, vh)
+
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": ms, "launches_timed": reps,
+            "schedule": "torch bmm (bf16) -> fp32 scale/mask -> softmax (fp32) -> bf16 P -> bmm",
+            "score_matrix_elements": hq * N * N}
+
+
+# ---------------------------------------------------------------------------
 # Decode (split-K/V) timing
 # ---------------------------------------------------------------------------
 
@@ -348,6 +390,10 @@ def main(argv=None):
     ap.add_argument("--fp8", action="store_true",
                     help="forward with FP8 (e4m3) Q, K, V (fa_fwd_fp8, V^T pre-pass included): "
                          "amax-scaled N(0, 1) inputs of the workload's shape")
+    ap.add_argument("--standard", action="store_true",
+                    help="also time the materialising schedule on the GPU with torch (S = QK^T "
+                         "to HBM, softmax to HBM, then P V), bf16 fixed-length forward only: "
+                         "context for the speedup of the tiled kernel, not a product path")
     ap.add_argument("--decode-batch", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -543,6 +589,12 @@ def main(argv=None):
     # Cold launches: a 512 MiB write between launches evicts Q, K, V from the
     # L2 caches and the 256 MB last-level cache; each launch is bracketed by
     # its own events.
+    standard = None
+    if args.standard and args.which == "fwd" and w.dtype == "bf16" and not w.packed and \
+            args.window < 0 and bias_t is None and fp8_x is None:
+        standard = standard_attention_ms(torch, q, k, v, w, stream)
+        standard["speedup_of_tiled_kernel"] = standard["ms"] / float(np.mean(per_launch_ms))
+
     cold_ms = []
     if args.cold_launches > 0:
         scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
@@ -619,6 +671,7 @@ def main(argv=None):
                           1 if args.bias == "shared" else B * w.hq)}
                      if bias_t is not None else None),
             "standard_path_bytes_avoided": standard_path_bytes_avoided(lens_q, w.hq),
+            "standard_schedule_on_gpu": standard,
             "launch_ms": {"mean": avg_launch_ms, "min": float(np.min(per_launch_ms)),
                           "median": float(np.median(per_launch_ms)),
                           "max": float(np.max(per_launch_ms))},
