@@ -68,7 +68,9 @@ constexpr float kRaise = 16.f;      // the main loop keeps m while the block max
 // this block (32 score registers per query tile) are spread evenly over the
 // first M - 2*ND steps; P V chunk g is placed right after the step that
 // finishes its 16 probabilities (8 per query tile), and score MFMAs fill the
-// remaining steps.
+// remaining steps. The last 2*ND steps (chunk 3's P V MFMAs) carry the row
+// maxima of the next block's scores, whose MFMAs are done by then, so the
+// next block starts with its reference update instead of a serial reduction.
 template <int D>
 struct Plan {
   static constexpr int NC = D / 16;
@@ -100,6 +102,13 @@ struct Plan {
     for (int s = 0; s < M; ++s)
       if (pv_chunk(s) < 0 && qk_index(s) == 2 * p) return s;
     return -1;
+  }
+  // last step that forms a score MFMA of key tile kt, query tile qt
+  static constexpr int last_qk_step(int kt, int qt) {
+    int last = -1;
+    for (int s = 0; s < M; ++s)
+      if (pv_chunk(s) < 0 && qk_index(s) / (2 * NC) == kt && qk_index(s) % 2 == qt) last = s;
+    return last;
   }
   static constexpr bool valid() {
     int qk = 0;
@@ -386,17 +395,33 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         }
       }
   }
+  // Row maxima of the next block's scores, formed ahead of it (unmasked
+  // blocks use them; masked ones form their own after the mask).
+  float nmax[2] = {-INFINITY, -INFINITY};
+  if constexpr (!BIAS) {
+    mfma_result_guard();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = sa[qt][0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[qt][0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[qt][1][r]);
+      nmax[qt] = xhalf_max(mx);
+    }
+  }
 
   // One key block j: its scores sc are in registers. On entry the loads of
   // K_{j+1} and V_j are in flight (issued one block earlier).
   //   head: wait for them, barrier (every wave is done with block j-1, so
   //      the buffers of K_j and V_{j-1} are free), start the loads of
   //      K_{j+2} and V_{j+1} into those buffers;
-  //   body: mask, row maxima, reference; then the M steps of Plan<D>: the
-  //      scores of block j+1 (sn) from K_{j+1}, the exponentials of block j,
-  //      and O^T += V_j^T P_j^T, one MFMA per step, so the matrix cores run
-  //      while the vector unit computes exponentials. Operands are read from
-  //      LDS kAhead steps early.
+  //   body: mask (then the row maxima of a masked block), reference; then
+  //      the M steps of Plan<D>: the scores of block j+1 (sn) from K_{j+1},
+  //      the exponentials of block j, and O^T += V_j^T P_j^T, one MFMA per
+  //      step, so the matrix cores run while the vector unit computes
+  //      exponentials; the last steps form the row maxima of sn. Operands
+  //      are read from LDS kAhead steps early.
   constexpr int kAhead = 2;
   auto head = [&](auto par_tag, int jb) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
@@ -418,7 +443,10 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     const unsigned char* v_cur = PAR ? vw1 : vw0;   // V_j
     if (jb >= nblk_w) return;
     const int k0 = key_base + jb * kBC;
-    mfma_result_guard();  // the last score MFMAs of sc may still be in flight
+    // the last score MFMAs of sc may still be in flight (without a bias the
+    // previous block's last steps already read every score register)
+    if constexpr (BIAS) mfma_result_guard();
+    bool masked = false;
 
     // LDS operands: score operand p (K tile p/NC, d-chunk p%NC) is first used
     // at step qk_first(p); value operand (t, g) at pv_start(g) + 2t.
@@ -441,6 +469,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     // 2^(c * -inf - m) = 0.
     if constexpr (!WIN) {
       if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0)) {
+        masked = true;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           const int qrow = wq0 + 32 * qt + j;
@@ -456,6 +485,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
       if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wq0) ||
           (p.win_left >= 0 && k0 < wq0 + 63 - p.win_left) ||
           (p.win_right >= 0 && k0 + kBC - 1 > wq0 + p.win_right)) {
+        masked = true;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           const int qrow = wq0 + 32 * qt + j;
@@ -491,14 +521,20 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     }
     float mb[2], smax[2];
     bool up = false;
+    if (BIAS || masked) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = fmaxf(sc[qt][0][0], sc[qt][0][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[qt][0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qt][1][r]);
+        nmax[qt] = xhalf_max(mx);
+      }
+    }
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float mx = fmaxf(sc[qt][0][0], sc[qt][0][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[qt][0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qt][1][r]);
-      smax[qt] = xhalf_max(mx);
+      smax[qt] = nmax[qt];
       mb[qt] = smax[qt] * ce;
       // A row's first visible block sets its reference (its accumulator and
       // denominator are still zero); later raises need the rescale.
@@ -541,6 +577,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     // chunk e/16, query tile (e/8)%2, slot e%8.
     float rs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     bf16x8 pb[2][4];
+    float tmax[2];
     static_for<PL::M>([&](auto S) {
       if constexpr (S + kAhead < PL::M) load_for_step(std::integral_constant<int, S + kAhead>{});
       constexpr int g = PL::pv_chunk(S);
@@ -555,6 +592,17 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
         acc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[g][t], pb[qt][g], acc[qt][t],
                                                              0, 0, 0);
         asm volatile("" : "+a"(acc[qt][t]));  // the accumulator lives in AGPRs
+      }
+      if constexpr (!BIAS && S >= PL::M - 2 * ND) {
+        // steps without exponentials: row maxima of the next block, a
+        // score tile (qt, kt) per ND/2 steps, kt = 0 first
+        constexpr int i = S - (PL::M - 2 * ND), spt = ND / 2;
+        constexpr int tt = i / spt, part = i % spt, qt = tt & 1, kt = tt >> 1;
+        constexpr int r0 = part * 16 / spt, r1 = (part + 1) * 16 / spt;
+        static_assert(kt == 0 || S - PL::last_qk_step(kt, qt) >= 4, "score results ready");
+        if constexpr (tt == 0 && part == 0) { tmax[0] = -INFINITY; tmax[1] = -INFINITY; }
+        static_for<r1 - r0>([&](auto R) { tmax[qt] = fmaxf(tmax[qt], sn[qt][kt][r0 + R]); });
+        if constexpr (kt == 1 && part == spt - 1) nmax[qt] = xhalf_max(tmax[qt]);
       }
       constexpr int e0 = PL::first_elem(S);
       static_for<PL::first_elem(S + 1) - e0>([&](auto EI) {
