@@ -177,8 +177,28 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
     const int hh = idx % gq;
     const int t2 = idx / gq;
     const int upx = units >> 3;
-    const int u = (t2 % upx) * 8 + x;
-    tile = n_qt - 1 - t2 / upx;
+    // With many tiles per unit (long sequences, whose K/V heads outgrow an
+    // L2), chunks of ch tiles of one unit (up to 32 workgroups, one XCD's
+    // CUs) run together, so the XCD streams one K/V head at a time. Chunks
+    // run longest first across the XCD's units, a partial chunk (n_qt % ch
+    // tiles) last; ch <= n_qt / 8 keeps the last chunks short. ch = 1 is
+    // plain longest-first order across units.
+    const int ch = n_qt >= 32 ? max(1, min(32 / gq, n_qt / 8)) : 1;
+    const int n_full = n_qt / ch;
+    const int full_slots = n_full * upx * ch;
+    int ui, rank;
+    if (t2 < full_slots) {
+      const int r2 = t2 / ch;
+      ui = r2 % upx;
+      rank = (r2 / upx) * ch + t2 % ch;
+    } else {
+      const int rem = n_qt - n_full * ch;
+      const int t3 = t2 - full_slots;
+      ui = t3 / rem;
+      rank = n_full * ch + t3 % rem;
+    }
+    const int u = ui * 8 + x;
+    tile = n_qt - 1 - rank;
     b = u / p.hkv;
     h = (u % p.hkv) * gq + hh;
   } else {

@@ -152,6 +152,8 @@ def test_workload5_shortest_longest_and_sampled():
     inp, o, lse = _run_nan_filled(5)
     o = o.float().cpu().double().numpy()
     lse = lse.cpu().double().numpy()
+    # every row sees at least its own key: an unwritten row stays NaN
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "workload 5: rows left unwritten"
     lens = np.asarray(inp.lens, dtype=np.int64)
     cu = inp.cu_seqlens.astype(np.int64)
     for s in sorted({int(np.argmin(lens)), int(np.argmax(lens))}):
