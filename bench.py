@@ -295,18 +295,27 @@ def decode_main(args, fa, torch, dev):
 
     for _ in range(args.warmup):
         step()
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # timed region: the K calls between two events; then up to 20 single
+    # calls, each between its own events, for their spread
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    events[0].record(stream)
+    e_start.record(stream)
     for i in range(args.steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    ms = e_start.elapsed_time(e_end) / args.steps
+    n_spread = min(args.steps, 20)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    events[0].record(stream)
+    for i in range(n_spread):
         step()
         events[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
-    ms = events[0].elapsed_time(events[-1]) / args.steps
+    per = [events[i].elapsed_time(events[i + 1]) for i in range(n_spread)]
     abytes = algorithmic_bytes(B, B * n, w.hq, w.hkv, w.d, 2)
     gbs = abytes / (ms * 1e-3) / 1e9
-    achieved = abytes / (float(np.mean(per)) * 1e-3) / 1e9
+    achieved = gbs  # the timed region holds nothing but the K calls
     ok = bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
     line = {
         "metric": f"attention decode GB/s (split-K/V, {B} sequences x {n} keys, "
@@ -321,8 +330,9 @@ def decode_main(args, fa, torch, dev):
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None},
         "detail": {"alg_hbm_bytes": abytes,
                    "alg_flops": algorithmic_flops([1] * B, [n] * B, w.hq, w.d, False),
-                   "launch_ms": {"mean": float(np.mean(per)), "min": float(np.min(per)),
-                                 "median": float(np.median(per))},
+                   "launch_ms": {"mean": ms, "single_call_min": float(np.min(per)),
+                                 "single_call_median": float(np.median(per)),
+                                 "single_calls": len(per)},
                    "outputs_finite": ok, "device": torch.cuda.get_device_name(dev)},
     }
     if not args.no_cpu_baseline:
@@ -572,19 +582,29 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K back-to-back launches on the stream they run on, with an
-    # event between consecutive launches for per-launch durations.
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Timed region: K back-to-back launches on the stream they run on, between
+    # two events (an event between launches adds a gap of several
+    # microseconds, a large share of a short launch).
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    events[0].record(stream)
+    e_start.record(stream)
     for i in range(args.steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = e_start.elapsed_time(e_end)
+    # Spread of single launches (not part of the timed region): up to 20 more
+    # launches, each between its own events.
+    n_spread = min(args.steps, 20)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    events[0].record(stream)
+    for i in range(n_spread):
         step()
         events[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
-    total_ms = events[0].elapsed_time(events[-1])
+    per_launch_ms = [events[i].elapsed_time(events[i + 1]) for i in range(n_spread)]
 
     # Cold launches: a 512 MiB write between launches evicts Q, K, V from the
     # L2 caches and the 256 MB last-level cache; each launch is bracketed by
@@ -593,7 +613,7 @@ def main(argv=None):
     if args.standard and args.which == "fwd" and w.dtype == "bf16" and not w.packed and \
             args.window < 0 and bias_t is None and fp8_x is None:
         standard = standard_attention_ms(torch, q, k, v, w, stream)
-        standard["speedup_of_tiled_kernel"] = standard["ms"] / float(np.mean(per_launch_ms))
+        standard["speedup_of_tiled_kernel"] = standard["ms"] / (total_ms / args.steps)
 
     cold_ms = []
     if args.cold_launches > 0:
@@ -622,7 +642,7 @@ def main(argv=None):
         tq, tk, w.hq, w.hkv, w.d, elem)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
-    avg_launch_ms = float(np.mean(per_launch_ms))
+    avg_launch_ms = ms_per_step  # the timed region holds nothing but the K launches
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     if fp8_x is not None:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
@@ -672,9 +692,11 @@ def main(argv=None):
                      if bias_t is not None else None),
             "standard_path_bytes_avoided": standard_path_bytes_avoided(lens_q, w.hq),
             "standard_schedule_on_gpu": standard,
-            "launch_ms": {"mean": avg_launch_ms, "min": float(np.min(per_launch_ms)),
-                          "median": float(np.median(per_launch_ms)),
-                          "max": float(np.max(per_launch_ms))},
+            "launch_ms": {"mean": avg_launch_ms,
+                          "single_launch_min": float(np.min(per_launch_ms)),
+                          "single_launch_median": float(np.median(per_launch_ms)),
+                          "single_launch_max": float(np.max(per_launch_ms)),
+                          "single_launches": len(per_launch_ms)},
             "cold_launch_ms": ({"median": float(np.median(cold_ms)), "min": float(np.min(cold_ms)),
                                 "launches": len(cold_ms)} if cold_ms else None),
             "host_wall_s": wall,

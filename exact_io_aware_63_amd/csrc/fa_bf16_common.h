@@ -131,15 +131,21 @@ __device__ __forceinline__ void issue_tile(const u16* g, long stride, int r0, in
   const uint32_t nrec = static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u16*>(g + static_cast<long>(r0) * stride), 0, nrec, kBufferFlags);
-#pragma unroll
-  for (int it = 0; it < T::kLoads; ++it) {
-    const int u = it * kThreads + tid;
+  // Wave w fills 1 KiB chunks w*kLoads .. w*kLoads + kLoads-1 of the tile
+  // from one LDS base (M0), the chunk's offset in the instruction offset
+  // field, which the hardware adds to the global offset as well.
+  static_assert(T::kLoads <= 4, "chunk offsets fit the 12-bit instruction offset");
+  const int lane = tid & 63;
+  unsigned char* const base = dst + w * (T::kLoads * 1024);
+  static_for<T::kLoads>([&](auto IT) {
+    constexpr int it = decltype(IT)::value;
+    const int u = (w * T::kLoads + it) * 64 + lane;
     const int row = u / T::kUnits;
     const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
-    const uint32_t voff = row * stride_b + gc * 16;
-    const int lds_off = (it * kThreads + w * 64) * 16;  // wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + lds_off), 16, voff, 0, 0, 0);
-  }
+    // >= 0: row >= 64 * it / kUnits and stride_b >= kRowBytes = 16 * kUnits
+    const uint32_t voff = row * stride_b + gc * 16 - it * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)base, 16, voff, 0, it * 1024, 0);
+  });
 }
 
 }  // namespace
