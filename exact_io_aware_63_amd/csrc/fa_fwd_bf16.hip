@@ -442,7 +442,7 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   //      step, so the matrix cores run while the vector unit computes
   //      exponentials; the last steps form the row maxima of sn. Operands
   //      are read from LDS kAhead steps early.
-  constexpr int kAhead = 2;
+  constexpr int kAhead = 3;
   auto head = [&](auto par_tag, int jb) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
     unsigned char* k_free = PAR ? kb1 : kb0;        // K_j, consumed
