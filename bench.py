@@ -281,6 +281,10 @@ def decode_main(args, fa, torch, dev):
     q, k, v = up(inp.q_bits), up(inp.k_bits), up(inp.v_bits)
     o = torch.empty_like(q)
     lse = torch.empty((B, w.hq, 1), dtype=torch.float32, device=dev)
+    if args.decode_splits <= 0:  # the library's recommendation for this device
+        args.decode_splits = fa.fa_fwd_splitkv_num_splits(B, w.hkv, n)
+        if args.decode_splits < 1:
+            raise RuntimeError(f"fa_fwd_splitkv_num_splits failed: {fa.fa_last_error()}")
     nbytes = fa.fa_fwd_splitkv_workspace_bytes(B, w.hq, 1, w.d, args.decode_splits)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -405,7 +409,8 @@ def main(argv=None):
                          "to HBM, softmax to HBM, then P V), bf16 fixed-length forward only: "
                          "context for the speedup of the tiled kernel, not a product path")
     ap.add_argument("--decode-batch", type=int, default=16)
-    ap.add_argument("--decode-splits", type=int, default=8)
+    ap.add_argument("--decode-splits", type=int, default=0,
+                    help="key ranges per (entry, K/V head); 0: fa_fwd_splitkv_num_splits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

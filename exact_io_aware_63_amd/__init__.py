@@ -84,6 +84,8 @@ _lib.fa_fwd_fp8_workspace_bytes.argtypes = [ctypes.c_int] * 3
 _lib.fa_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_fwd_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 5
 _lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+_lib.fa_fwd_splitkv_num_splits.argtypes = [ctypes.c_int] * 4
+_lib.fa_fwd_splitkv_num_splits.restype = ctypes.c_int
 _lib.fa_status_string.argtypes = [ctypes.c_int]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
@@ -95,7 +97,8 @@ _lib.fa_version.restype = ctypes.c_int
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
             "fa_bwd_bias",
-            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_noalloc",
+            "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_num_splits",
+            "fa_fwd_splitkv_noalloc",
             "fa_fwd_fp8",
             "fa_fwd_fp8_workspace_bytes", "fa_check_cu_seqlens", "fa_status_string",
             "fa_last_error", "fa_version")
@@ -182,6 +185,11 @@ def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal
 def fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:
     """C ``fa_fwd_splitkv_workspace_bytes``."""
     return _lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+
+
+def fa_fwd_splitkv_num_splits(B, Hkv, Nk, num_cus=0) -> int:
+    """C ``fa_fwd_splitkv_num_splits``: a split count (>= 1) or a negative status."""
+    return _lib.fa_fwd_splitkv_num_splits(B, Hkv, Nk, num_cus)
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale,

@@ -524,6 +524,20 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_spli
   return decode_workspace(B, Hq, Nq, d, num_splits);
 }
 
+int fa_fwd_splitkv_num_splits(int B, int Hkv, int Nk, int num_cus) {
+  g_last_error[0] = '\0';
+  if (B < 1 || Hkv < 1 || Nk < 1)
+    return fail(FA_ERR_SHAPE, "B=%d, Hkv=%d and Nk=%d must all be at least 1", B, Hkv, Nk);
+  if (num_cus <= 0) {
+    const int st = check_device(&num_cus);
+    if (st != FA_OK) return st;
+  }
+  const int64_t units = static_cast<int64_t>(B) * Hkv;
+  const int64_t want = (3 * static_cast<int64_t>(num_cus) + units / 2) / units;
+  const int64_t cap = std::min<int64_t>(1024, std::max<int64_t>(1, Nk / 512));
+  return static_cast<int>(std::max<int64_t>(1, std::min(want, cap)));
+}
+
 int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                    int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                    const int32_t* seqlens_k, int num_splits, void* workspace,

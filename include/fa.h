@@ -236,6 +236,17 @@ int fa_bwd_bias(const void* Q, const void* K, const void* V, const void* O,
  * Nq == 0 is a no-op. Other arguments and errors as fa_fwd.
  */
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits);
+
+/*
+ * A split count for fa_fwd_splitkv: enough key ranges that the split pass
+ * fills about three workgroups per compute unit, round(3 * num_cus / (B *
+ * Hkv)), clamped to 1 .. min(1024, max(1, Nk / 512)) so that a range keeps
+ * at least 512 keys. num_cus <= 0 takes the current device's count. Returns
+ * the count (>= 1), or a negative FA_ERR_* (B, Hkv or Nk < 1: FA_ERR_SHAPE;
+ * no usable device when num_cus <= 0: as fa_fwd). Host only; launches
+ * nothing.
+ */
+int fa_fwd_splitkv_num_splits(int B, int Hkv, int Nk, int num_cus);
 int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O,
                    float* LSE, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                    float scale, int causal, const int32_t* seqlens_k,

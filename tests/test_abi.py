@@ -28,8 +28,8 @@ def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_fp32", "fa_fwd_window", "fa_fwd_bias", "fa_bwd", "fa_bwd_window",
          "fa_bwd_bias", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes",
-         "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_noalloc", "fa_check_cu_seqlens",
-         "fa_status_string", "fa_last_error", "fa_version"])
+         "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_noalloc",
+         "fa_check_cu_seqlens", "fa_status_string", "fa_last_error", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -490,3 +490,15 @@ def test_noalloc_rejects_calls_beyond_its_scratch(fa):
                                        (dict(B=0), 0), (dict(Nq=0), 0)])
 def test_noalloc_shares_the_host_checks(fa, kw, status):
     assert _call_noalloc(fa, **kw) == status, fa.fa_last_error()
+
+
+def test_splitkv_num_splits(fa):
+    """About three split workgroups per compute unit, each range >= 512 keys."""
+    assert fa.fa_fwd_splitkv_num_splits(16, 8, 8192, 256) == 6     # 768 / 128
+    assert fa.fa_fwd_splitkv_num_splits(1, 8, 8192, 256) == 16     # 96 capped by 8192 / 512
+    assert fa.fa_fwd_splitkv_num_splits(2, 1, 1 << 20, 256) == 384  # 768 / 2
+    assert fa.fa_fwd_splitkv_num_splits(1, 1, 1 << 30, 1024) == 1024
+    assert fa.fa_fwd_splitkv_num_splits(64, 32, 8192, 256) == 1    # more units than slots
+    assert fa.fa_fwd_splitkv_num_splits(4, 8, 300, 256) == 1       # fewer than 512 keys
+    for bad in ((0, 8, 8192), (4, 0, 8192), (4, 8, 0)):
+        assert fa.fa_fwd_splitkv_num_splits(*bad, 256) == fa.FA_ERR_SHAPE
