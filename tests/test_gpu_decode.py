@@ -113,3 +113,27 @@ def test_splitkv_matches_fwd():
     torch.cuda.synchronize()
     assert max_err(o1.float().cpu().numpy(), o2.float().cpu().numpy()) <= TOL_O["bf16"]
     assert max_err(l1.cpu().numpy(), l2.cpu().numpy()) <= TOL_LSE["bf16"]
+
+
+def test_splitkv_recommended_splits_parity():
+    """The split count the library recommends for this device (used by the
+    decode benchmark) on a bench-like decode shape with ragged lengths."""
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    b, hq, hkv, nk, d = 16, 32, 8, 2048, 128
+    n = fa.fa_fwd_splitkv_num_splits(b, hkv, nk, 0)
+    say(f"[case] splitkv recommended splits: {n}")
+    assert 1 <= n <= 1024
+    lens = [nk - 97 * i for i in range(b)]
+    inp = W.draw(b, hq, hkv, 1, nk, d, "bf16", seed=4242)
+    scale = 1.0 / math.sqrt(d)
+    sk = torch.tensor(lens, dtype=torch.int32).cuda()
+    o, lse = fa.attention_fwd_splitkv(_dev(inp.q_bits), _dev(inp.k_bits), _dev(inp.v_bits),
+                                      num_splits=n, causal=False, scale=scale, seqlens_k=sk)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _reference(inp, lens, scale, False)
+    eo = max_err(o.float().cpu().double().numpy(), o_ref)
+    el = max_err(lse.cpu().double().numpy(), lse_ref)
+    say(f"[parity] recommended splits {n}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE["bf16"]
