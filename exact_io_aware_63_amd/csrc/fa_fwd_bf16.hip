@@ -335,14 +335,24 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // S^T = K Q^T (column = query, 8 consecutive d values per lane). Query
   // tile qt of this wave covers rows wq0 + 32qt .. +31; this lane's row is
   // wq0 + 32qt + j.
+  // All loads are issued before any is used (a row past the end reads the
+  // last row, then its fragment is zeroed), so the wave waits for memory
+  // once instead of once per load.
   bf16x8 qf[2][NC];
+  u32x4 qv[2][NC];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const int qrow = wq0 + 32 * qt + j;
+    const int qrow = min(wq0 + 32 * qt + j, Lq - 1);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      qv[qt][cc] = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2);
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const bool live = wq0 + 32 * qt + j < Lq;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow < Lq) v = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2) ^ qflip;
+      const u32x4 v = live ? (qv[qt][cc] ^ qflip) : u32x4{0u, 0u, 0u, 0u};
       qf[qt][cc] = as_bf16x8(v);
       asm volatile("" : "+a"(qf[qt][cc]));  // move to an AGPR now
     }
