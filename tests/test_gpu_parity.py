@@ -167,3 +167,35 @@ def test_workload5_shortest_longest_and_sampled():
     o_ref, lse_ref = oracle.attention_picked(inp.q, inp.k, inp.v, w.scale, w.causal, picks,
                                              cu_seqlens=inp.cu_seqlens)
     assert_parity(og, lg, o_ref, lse_ref, "bf16", f"workload 5 ({len(picks)} sampled rows)")
+
+
+@pytest.mark.timeout(600)
+def test_packed_chunked_order_partial_chunk():
+    """Packed sequences long enough for the chunked tile order (33 query
+    tiles of the longest, 16 units: two per XCD, chunks of 4 tiles and a
+    partial chunk of 1): every row is written, and sampled rows of both
+    sequences match the oracle."""
+    import torch
+
+    import exact_io_aware_63_amd as fa
+    lens = [8448, 5000]
+    hq = hkv = 8
+    d = 64
+    say(f"[case] packed chunked order: lens {lens}, H {hq}, d {d}")
+    inp = W.draw(2, hq, hkv, 0, 0, d, "bf16", seed=808, lens=lens)
+    q, k, v, cu = to_device(inp)
+    o0 = torch.full_like(q, float("nan"))
+    l0 = torch.full((hq, q.shape[0]), float("nan"), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=True, scale=scale, cu_seqlens=cu,
+                              max_seqlen=max(lens), out=o0, lse=l0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all()), \
+        "rows left unwritten"
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    picks = pick_rows(inp, 256, seed=808, hq=hq)
+    og, lg = gather_picks(o, lse, picks, inp)
+    o_ref, lse_ref = oracle.attention_picked(inp.q, inp.k, inp.v, scale, True, picks,
+                                             cu_seqlens=inp.cu_seqlens)
+    assert_parity(og, lg, o_ref, lse_ref, "bf16", f"packed chunked order ({len(picks)} rows)")
