@@ -56,6 +56,30 @@ namespace fa {
 namespace {
 
 constexpr int kBR = kBf16TileRows;  // query rows per workgroup
+
+// issue_tile for a tile that may not be wanted: an unwanted tile gets an
+// empty buffer range (its loads read nothing and write zeros to its LDS),
+// so every wave issues the same number of loads either way.
+template <int D>
+__device__ __forceinline__ void issue_tile_if(const u16* g, long stride, int r0, int L, bool want,
+                                              unsigned char* dst, int tid, int w) {
+  using T = Tile<D>;
+  const int rows = min(L - r0, kTileRows);
+  const uint32_t stride_b = static_cast<uint32_t>(stride * 2);
+  const uint32_t nrec = want ? static_cast<uint32_t>(rows - 1) * stride_b + T::kRowBytes : 0u;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g + static_cast<long>(want ? r0 : 0) * stride), 0, nrec, kBufferFlags);
+  const int lane = tid & 63;
+  unsigned char* const base = dst + w * (T::kLoads * 1024);
+  static_for<T::kLoads>([&](auto IT) {
+    constexpr int it = decltype(IT)::value;
+    const int u = (w * T::kLoads + it) * 64 + lane;
+    const int row = u / T::kUnits;
+    const int gc = (u % T::kUnits) ^ swz<T::kUnits>(row);
+    const uint32_t voff = row * stride_b + gc * 16 - it * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)base, 16, voff, 0, it * 1024, 0);
+  });
+}
 constexpr int kBC = kTileRows;      // keys per K/V block
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRaise = 16.f;      // the main loop keeps m while the block max is <= m + 16
@@ -153,6 +177,10 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[NH * T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[NH * T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb1[NH * T::kBytes];
+  // the workgroup's Q rows, staged once (a smaller alignment places them
+  // after the K/V buffers, whose LDS offsets then fit the 16-bit immediate
+  // of the key loop's LDS reads)
+  __shared__ __attribute__((aligned(256))) unsigned char qst[(ROWS / 64) * T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,14 +300,24 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // Every tile is loaded by all four waves; hk(h) is the first key of
   // half h, and a half streams nbh[h] blocks.
   auto hk = [&](int h) { return SPLIT ? h * nblk * kBC : key_base; };
+  // K_0 and the workgroup's Q rows first, then V_0 and K_1: a fixed number
+  // of loads per wave, so the first scores wait for the first group only.
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    issue_tile_if<D>(kg, kstride, hk(h), Lk, nbh[h] > 0, kb0 + h * T::kBytes, tid, w);
+#pragma unroll
+  for (int sub = 0; sub < ROWS / 64; ++sub)
+    issue_tile_if<D>(qg, qstride, q0 + 64 * sub, Lq, q0 + 64 * sub < Lq, qst + sub * T::kBytes,
+                     tid, w);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    if (nbh[h] > 0) {
-      issue_tile<D>(kg, kstride, hk(h), Lk, kb0 + h * T::kBytes, tid, w);
-      issue_tile<D>(vg, kstride, hk(h), Lk, vb0 + h * T::kBytes, tid, w);
-      if (nbh[h] > 1) issue_tile<D>(kg, kstride, hk(h) + kBC, Lk, kb1 + h * T::kBytes, tid, w);
-    }
+    issue_tile_if<D>(vg, kstride, hk(h), Lk, nbh[h] > 0, vb0 + h * T::kBytes, tid, w);
+    issue_tile_if<D>(kg, kstride, hk(h) + kBC, Lk, nbh[h] > 1, kb1 + h * T::kBytes, tid, w);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kLater = NH * 2 * T::kLoads;  // loads issued after K_0 and Q
+  static_assert(kLater <= 63, "vmcnt range");
   // this wave's view of the buffers (its key half)
   unsigned char* const kw0 = kb0 + half * T::kBytes;
   unsigned char* const kw1 = kb1 + half * T::kBytes;
@@ -335,17 +373,29 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // S^T = K Q^T (column = query, 8 consecutive d values per lane). Query
   // tile qt of this wave covers rows wq0 + 32qt .. +31; this lane's row is
   // wq0 + 32qt + j.
-  // All loads are issued before any is used (a row past the end reads the
-  // last row, then its fragment is zeroed), so the wave waits for memory
-  // once instead of once per load.
+  // They are read from the staged rows once this wave's K_0 and Q loads are
+  // done (at most kLater of its loads still in flight) and the barrier has
+  // made every wave's part visible. The barrier is a bare one: the fence of
+  // __syncthreads would also wait for V_0 and K_1. A row past the end is
+  // zero in LDS and its fragment is zeroed again below.
   bf16x8 qf[2][NC];
   u32x4 qv[2][NC];
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLater) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  {
+    const unsigned char* qs = qst + wrow * T::kBytes;  // rows wq0 .. wq0+63
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int qrow = min(wq0 + 32 * qt + j, Lq - 1);
+    for (int qt = 0; qt < 2; ++qt) {
+      const int row = 32 * qt + j;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-      qv[qt][cc] = ld16(qg + static_cast<long>(qrow) * qstride + 16 * cc + 8 * h2);
+      for (int cc = 0; cc < NC; ++cc) {
+        const int unit = (2 * cc + h2) ^ swz<T::kUnits>(row);
+        qv[qt][cc] = *reinterpret_cast<const u32x4*>(qs + row * T::kRowBytes + unit * 16);
+      }
+    }
   }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -410,8 +460,6 @@ void fwd_bf16_kernel(FwdParams p, int n_qt) {
   // S^T of one block: s[qt][kt][r] is the score of key
   // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query wq0 + 32qt + j.
   f32x16 sa[2][2], sb[2][2];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   if (nblk_w > 0) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
