@@ -90,12 +90,10 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Score MFMAs (S^T tile = K operand x Q fragment) as inline asm, with the
-// Q fragment in AGPRs and the scores written to AGPRs. The compiler does
-// not see these as MFMAs, so it must never touch a score tile before the
-// result is written: the tile is an AGPR output that nothing reads until
-// read_agpr(), which follows mfma8_result_guard() at the end of the region
-// and moves the scores to VGPRs, where the next block's vector work reads
-// them.
+// Q fragment in AGPRs and the scores written to VGPRs, where the next
+// block's vector work reads them. The compiler does not see these as
+// MFMAs, so nothing reads a score tile before mfma8_result_guard() at the
+// end of the region that formed it.
 __device__ __forceinline__ f32x16 mfma8_qk_first(i32x8 a, i32x8 b) {
   f32x16 d;
   asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
@@ -327,8 +325,9 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
 
   // S^T of one block from the K tile ks: s[qt][kt][r] is key
   // k0 + 32kt + 8(r/4) + 4*h2 + (r%4) against query wq0 + 32qt + j.
-  f32x16 s_ag[2][2];  // score MFMA outputs (AGPRs)
-  f32x16 sv[2][2];    // scores of the next block to process (VGPRs)
+  // two score sets: a block reads its scores from one while its region forms
+  // the next block's in the other (the key loop swaps them)
+  f32x16 sa[2][2], sb[2][2];
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (nblk_w > 0) {
@@ -338,15 +337,11 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
       const i32x8 a1 = k_operand(kb[0], kt, 1);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        s_ag[qt][kt] = mfma8_qk_first(a0, qf[qt][0]);
-        mfma8_qk_acc(s_ag[qt][kt], a1, qf[qt][1]);
+        sa[qt][kt] = mfma8_qk_first(a0, qf[qt][0]);
+        mfma8_qk_acc(sa[qt][kt], a1, qf[qt][1]);
       }
     }
     mfma8_result_guard();
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = s_ag[qt][kt];
   }
 
   // One key block j; its scores sc are in registers and the loads of
@@ -368,13 +363,12 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
     if (jb + 1 < nblk)
       issue_vt(vtg + static_cast<long>(jb + 1) * kVtBytes, vb[PAR ^ 1], tid, w);
   };
-  auto body = [&](auto par_tag, int jb) {
+  auto body = [&](auto par_tag, int jb, f32x16(&sc)[2][2], f32x16(&sn)[2][2]) {
     constexpr int PAR = decltype(par_tag)::value;  // jb & 1
     if (jb >= nblk_w) return;
     const int k0 = jb * kBlk;
     const unsigned char* k_next = kb[PAR ^ 1];  // K_{j+1}
     const unsigned char* v_cur = vb[PAR];       // V^T_j
-    f32x16 (&sc)[2][2] = sv;  // this block's scores, read out by the previous region
     // Mask the blocks that reach past the keys or cross this wave's diagonal.
     if ((k0 + kBlk > Lk) || (CAUSAL && k0 + kBlk - 1 > wq0)) {
 #pragma unroll
@@ -463,8 +457,8 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
       if constexpr (s + 2 < 16) loads_for(std::integral_constant<int, s + 2>{});
       if constexpr (s < 8) {
         constexpr int kt = s >> 2, cc = (s >> 1) & 1, qt = s & 1;
-        if constexpr (cc == 0) s_ag[qt][kt] = mfma8_qk_first(kop[kt][0], qf[qt][0]);
-        else mfma8_qk_acc(s_ag[qt][kt], kop[kt][1], qf[qt][1]);
+        if constexpr (cc == 0) sn[qt][kt] = mfma8_qk_first(kop[kt][0], qf[qt][0]);
+        else mfma8_qk_acc(sn[qt][kt], kop[kt][1], qf[qt][1]);
       } else {
         constexpr int qt = s >= 12 ? 1 : 0, tt = s - 8 - 4 * qt;
         const i32x8 pb = {pw[qt][0], pw[qt][1], pw[qt][2], pw[qt][3],
@@ -481,12 +475,9 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
     });
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) l_run[qt] += ldexpf(rs[qt][0] + rs[qt][1], tq[qt] - 8);
-    // the next block's scores, after the score MFMAs of this region finished
+    // the next block's scores are read only after the score MFMAs of this
+    // region have finished
     mfma8_result_guard();
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sv[qt][kt] = s_ag[qt][kt];
   };
 
   // Key loop, unrolled by two so every LDS address has a fixed buffer. A
@@ -496,10 +487,10 @@ void fwd_fp8_kernel(Fp8Params p, int n_qt) {
   using P1 = std::integral_constant<int, 1>;
   for (int jb = 0; jb < nblk; jb += 2) {
     head(P0{}, jb);
-    body(P0{}, jb);
+    body(P0{}, jb, sa, sb);
     if (jb + 1 >= nblk) break;
     head(P1{}, jb + 1);
-    body(P1{}, jb + 1);
+    body(P1{}, jb + 1, sb, sa);
   }
 
   // Epilogue: o = dv * a / l, rounded once to bf16; LSE = ln 2 (m + log2 l).
