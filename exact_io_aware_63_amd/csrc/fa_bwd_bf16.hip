@@ -470,13 +470,28 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
         d4[g4] = *reinterpret_cast<const float4*>(dsm + 32 * sub + 8 * g4 + 4 * h2);
       };
       load_ld(0, 0);
-      // phase 1: S and dP of sub-block 0
-      f32x16 s0 = mfma_qk_first(row_operand<D>(qs, 0, 0, lane), kf[0]);
-      f32x16 p0 = mfma_qk_first(row_operand<D>(ds_, 0, 0, lane), vf[0]);
-#pragma unroll
-      for (int cc = 1; cc < NC; ++cc) {
-        mfma_qk_acc(s0, row_operand<D>(qs, 0, cc, lane), kf[cc]);
-        mfma_qk_acc(p0, row_operand<D>(ds_, 0, cc, lane), vf[cc]);
+      // phase 1: S and dP of sub-block 0, operands read two steps ahead
+      f32x16 s0, p0;
+      {
+        bf16x8 op0[NS];
+        auto load_op0 = [&](int k) {
+          op0[k] = row_operand<D>((k & 1) ? ds_ : qs, 0, k >> 1, lane);
+        };
+        load_op0(0);
+        load_op0(1);
+        static_for<NS>([&](auto K) {
+          constexpr int k = decltype(K)::value;
+          if constexpr (k + 2 < NS) load_op0(k + 2);
+          constexpr int cc = k >> 1;
+          if constexpr ((k & 1) == 0) {
+            if constexpr (cc == 0) s0 = mfma_qk_first(op0[k], kf[0]);
+            else mfma_qk_acc(s0, op0[k], kf[cc]);
+          } else {
+            if constexpr (cc == 0) p0 = mfma_qk_first(op0[k], vf[0]);
+            else mfma_qk_acc(p0, op0[k], vf[cc]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       mfma_result_guard();
       // phase 2: S and dP of sub-block 1 on the matrix cores, P and dS of
@@ -551,19 +566,33 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, int n_kt, int 
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      // phase 4: dV and dK of sub-block 1
+      // phase 4: dV and dK of sub-block 1; transposed operands two steps
+      // ahead, the first two read before the mask and the packing
+      bf16x8 top1[NP];
+      auto load_top1 = [&](int k) {
+        const int g = k / (2 * ND), t = (k >> 1) % ND;
+        top1[k] = tr_operand<D>((k & 1) ? qs : ds_, 32, t, g, lane);
+      };
+      load_top1(0);
+      load_top1(1);
       if (!full1) mask_sub(1, s1, p1);
+      bf16x8 pb1[2], sbv1[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const bf16x8 pb = pack_chunk(s1, g);
-        const bf16x8 sbv = pack_chunk(p1, g);
-#pragma unroll
-        for (int t = 0; t < ND; ++t) {
-          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ds_, 32, t, g, lane), pb, dv[t], 0, 0, 0);
-          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, 32, t, g, lane), sbv, dk[t], 0, 0, 0);
-          asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
-        }
+        pb1[g] = pack_chunk(s1, g);
+        sbv1[g] = pack_chunk(p1, g);
       }
+      static_for<NP>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NP) load_top1(k + 2);
+        constexpr int g = k / (2 * ND), t = (k >> 1) % ND;
+        if constexpr ((k & 1) == 0)
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top1[k], pb1[g], dv[t], 0, 0, 0);
+        else
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top1[k], sbv1[g], dk[t], 0, 0, 0);
+        asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     const bool act0 = active(0), act1 = active(1);
     if constexpr (!BIAS) {
@@ -815,13 +844,26 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
       constexpr int NP = 2 * ND;   // product steps: 2 chunks x ND tiles
       constexpr int EPS = 16 / NS, EPP = 16 / NP;
       static_assert(EPS * NS == 16 && EPP * NP == 16, "element spread");
-      // phase 1: S^T and dP^T of sub-block 0
-      f32x16 s0 = mfma_qk_first(row_operand<D>(ks, 0, 0, lane), qf[0]);
-      f32x16 p0 = mfma_qk_first(row_operand<D>(vs, 0, 0, lane), dof[0]);
-#pragma unroll
-      for (int cc = 1; cc < NC; ++cc) {
-        mfma_qk_acc(s0, row_operand<D>(ks, 0, cc, lane), qf[cc]);
-        mfma_qk_acc(p0, row_operand<D>(vs, 0, cc, lane), dof[cc]);
+      // phase 1: S^T and dP^T of sub-block 0, operands read two steps ahead
+      f32x16 s0, p0;
+      {
+        bf16x8 op0[NS];
+        auto load_op0 = [&](int k) { op0[k] = row_operand<D>((k & 1) ? vs : ks, 0, k >> 1, lane); };
+        load_op0(0);
+        load_op0(1);
+        static_for<NS>([&](auto K) {
+          constexpr int k = decltype(K)::value;
+          if constexpr (k + 2 < NS) load_op0(k + 2);
+          constexpr int cc = k >> 1;
+          if constexpr ((k & 1) == 0) {
+            if constexpr (cc == 0) s0 = mfma_qk_first(op0[k], qf[0]);
+            else mfma_qk_acc(s0, op0[k], qf[cc]);
+          } else {
+            if constexpr (cc == 0) p0 = mfma_qk_first(op0[k], dof[0]);
+            else mfma_qk_acc(p0, op0[k], dof[cc]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       mfma_result_guard();
       // phase 2: sub-block 1's chains with sub-block 0's dS^T
@@ -865,17 +907,24 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int n_qt, int bi
         for (int e = 0; e < EPP; ++e) dscore_elem(k * EPP + e, s1, p1);
         __builtin_amdgcn_sched_barrier(0);
       });
-      // phase 4: sub-block 1's product
+      // phase 4: sub-block 1's product; transposed operands two steps
+      // ahead, the first two read before the mask and the packing
+      bf16x8 top1[NP];
+      auto load_top1 = [&](int k) { top1[k] = tr_operand<D>(ks, 32, k % ND, k / ND, lane); };
+      load_top1(0);
+      load_top1(1);
       if (!full1) mask_sub(1, p1);
+      bf16x8 sbv1[2];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const bf16x8 sbv = pack_chunk(p1, g);
-#pragma unroll
-        for (int t = 0; t < ND; ++t) {
-          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, 32, t, g, lane), sbv, dq[t], 0, 0, 0);
-          asm volatile("" : "+a"(dq[t]));
-        }
-      }
+      for (int g = 0; g < 2; ++g) sbv1[g] = pack_chunk(p1, g);
+      static_for<NP>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if constexpr (k + 2 < NP) load_top1(k + 2);
+        constexpr int g = k / ND, t = k % ND;
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(top1[k], sbv1[g], dq[t], 0, 0, 0);
+        asm volatile("" : "+a"(dq[t]));
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     const bool act0 = active(0), act1 = active(1);
     if constexpr (!BIAS) {
